@@ -1,0 +1,241 @@
+/*
+ * ra_kv.h -- paged, quantized-KV decode/verify attention for AMD MI355X (gfx950).
+ *
+ * C ABI of libra_kv.so.  Three operations make up one decode/verify step of a
+ * serving engine's attention layer:
+ *
+ *   ra_kv_store     quantise this step's new K/V rows and scatter them into
+ *                   16-token pages of the KV cache;
+ *   ra_paged_attn   attention of each sequence's query block (1 + k verify
+ *                   tokens, causal inside the block, grouped query heads) over
+ *                   its paged, quantised context, optionally split into KV
+ *                   partitions that emit partial (out, lse) pairs;
+ *   ra_lse_merge    combine partial (out, lse) pairs by log-sum-exp.
+ *
+ * Sources of the operations (the ReVolta pages):
+ *   - ReVolta README, intro list and "Weight and KV formats": the KV cache is
+ *     stored as FP8 E4M3, FP16 or INT8 and converted to FP16 for the
+ *     arithmetic; E4M3 uses calibrated per-layer K and V scales and strict mode
+ *     refuses to run without them.
+ *   - "ReVolta 0.1.3" release notes, "Known issues": 16-token kernel pages.
+ *   - ReVolta README, intro list and "Quick start": MTP4 verifies 1 + 4 tokens
+ *     per sequence per step; prefix caching shares pages between sequences;
+ *     decode context parallelism (DCP2) splits one sequence's context and
+ *     combines the parts' partial attention.
+ *   - ReVolta README, "DFlash2 speculative decoding", and "ReVolta 0.1.3",
+ *     "Behaviour changes": sliding-window and attention-sink layers.
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless marked (host).  The caller owns every
+ *     buffer; the library never allocates or frees memory, never synchronises,
+ *     and keeps no state other than a thread-local error message.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     the call returns at once.  Calls are safe from several host threads.
+ *   - Every condition checkable on the host is checked BEFORE anything is
+ *     enqueued.  On failure a non-zero ra_status is returned, ra_last_error()
+ *     describes it, and no output byte is changed.
+ *   - Conditions on device-resident data (block-table entries, context and
+ *     query lengths, slots) cannot be checked on the host.  The kernels never
+ *     read or write out of bounds because of them: an attention row whose
+ *     sequence violates them is written as NaN (out and lse), and a store
+ *     slot outside the cache is skipped.
+ *   - Attention results are deterministic and, for each sequence, bitwise
+ *     independent of the other sequences in the batch and of the batch size.
+ *
+ * Paged KV cache layout (identifier RA_KV_LAYOUT_ID)
+ *   K and V are separate caches.  Each holds num_pages * Hkv blocks of
+ *   16 * D * e bytes (e = 2 for FP16, 1 for E4M3 and INT8); block (page, head)
+ *   starts at byte (page * Hkv + head) * 16 * D * e.  Within a block, element
+ *   (t, d) -- token t of the page (0..15), dimension d -- is at byte
+ *       offset = (b / 16) * 1024 + lane * 16 + (b % 16)
+ *   with
+ *       K:  lane = 16 * (d / (D/4)) + t,          b = (d % (D/4)) * e
+ *       V:  lane = 16 * (t / 4) + d / (D/16),     b = ((d % (D/16)) * 4 + t % 4) * e
+ *   Elements are little-endian FP16 bit patterns, E4M3 bytes or two's-complement
+ *   int8.  A token's slot is page * 16 + t.  (Each 1 KiB of a block is one
+ *   64-lane x 16-byte load of a wavefront and lands in registers already in
+ *   the operand order of the gfx950 16x16x32 f16 matrix instruction.)
+ *
+ * Codes (the store's quantiser; bit-exact)
+ *   y = fp32(x) / fp32(scale), IEEE correctly rounded (x is the fp16/bf16 input);
+ *   E4M3 (OCP E4M3FN, bias 7, max 448): saturate to +-448 (+-inf -> +-448),
+ *     round to nearest, ties to even code, sign of y kept (-0 -> 0x80),
+ *     NaN -> 0x7F | sign;
+ *   INT8: round half to even, clamp to [-127, 127], NaN -> 0;
+ *   FP16 cache: IEEE round-to-nearest-even of fp32(x), no scale.
+ *   Dequantised value = fp32(decode(code)) * fp32(scale).
+ */
+#ifndef RA_KV_H_
+#define RA_KV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RA_KV_ABI_VERSION 1
+#define RA_KV_LAYOUT_ID 1
+#define RA_KV_PAGE_SIZE 16
+#define RA_KV_MAX_SPLITS 4096
+
+/* Status codes (int32_t return value of every entry point). */
+enum {
+  RA_OK = 0,
+  RA_ERR_INVALID_ARG = 1,   /* null pointer, bad size, inconsistent argument  */
+  RA_ERR_UNSUPPORTED = 2,   /* head_dim not 64/128, page size not 16, dtype   */
+  RA_ERR_MISALIGNED = 3,    /* a pointer or stride breaks 16-byte alignment   */
+  RA_ERR_WORKSPACE = 4,     /* partial buffers missing or too small           */
+  RA_ERR_HIP = 5            /* the HIP runtime refused the launch             */
+};
+
+/* Activation dtypes (queries, new K/V, attention output). */
+enum { RA_F16 = 1, RA_BF16 = 2, RA_F32 = 3 };
+
+/* KV cache element formats. */
+enum { RA_KV_F16 = 1, RA_KV_FP8_E4M3 = 2, RA_KV_INT8 = 3 };
+
+/*
+ * ra_kv_store -- quantise new K/V rows and scatter them into the paged caches.
+ *
+ * k, v          [num_tokens][num_kv_heads][head_dim] of src_dtype (RA_F16 or
+ *               RA_BF16); the token stride is k_token_stride / v_token_stride
+ *               ELEMENTS (so K/V may be views into a fused QKV buffer), heads
+ *               are head_dim apart, dims contiguous.  16-byte aligned, strides
+ *               multiples of 8.
+ * slot_mapping  int64 [num_tokens]; slot = page * 16 + token-in-page.  slot < 0
+ *               skips the token (padding).  Slots >= num_pages * 16 are
+ *               skipped.  Slots must be unique within one call.
+ * k_cache, v_cache  caches in the layout above, kv_dtype elements, 16-byte
+ *               aligned, num_pages * num_kv_heads * 16 * head_dim elements each.
+ * k_scale, v_scale  (host) per-layer scales; required finite and > 0 for
+ *               E4M3 / INT8 (there is no fallback to 1.0), ignored for FP16.
+ * head_dim in {64, 128}; page_size must be 16.
+ * Bytes of tokens not stored are left unchanged.
+ */
+int32_t ra_kv_store(const void* k, const void* v, int32_t src_dtype,
+                    int64_t k_token_stride, int64_t v_token_stride,
+                    const int64_t* slot_mapping, int64_t num_tokens,
+                    void* k_cache, void* v_cache, int32_t kv_dtype,
+                    int64_t num_pages, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t page_size, float k_scale, float v_scale, void* stream);
+
+/*
+ * Arguments of ra_paged_attn.  Set struct_size = sizeof(ra_attn_args).
+ *
+ * For sequence b: q_len_b = query_start_loc[b+1] - query_start_loc[b] and
+ * ctx_b = context_lens[b], which INCLUDES this step's q_len_b tokens (store
+ * them first).  Query i of the block sits at position pos = ctx_b - q_len_b + i;
+ * query head h reads KV head h / (num_q_heads / num_kv_heads).  Key j is
+ * visible iff j <= pos and (window_left < 0 or pos - j < window_left or
+ * j < num_sinks).  out = softmax(softmax_scale * q . k) v over visible keys,
+ * lse = natural log of the softmax denominator (max-shifted form); a row with
+ * no visible key gets out = 0, lse = -inf.
+ *
+ * Splitting: the keys of sequence b are cut into partitions of P_b tokens;
+ * num_splits = S > 0 gives P_b = 16 * ceil(ceil(ctx_b / S) / 16) (S slots per
+ * sequence); num_splits = 0 uses a fixed partition size chosen by the library
+ * from the call's constants only (see ra_paged_attn_workspace).  With more than
+ * one partition slot the kernel writes partial_out [slots][total_q][Hq][D] and
+ * partial_lse [slots][total_q][Hq] (fp32; out already normalised; an empty
+ * partition writes out = 0, lse = -inf) and, if `out` is non-NULL, merges them
+ * into out / lse on the same stream.  With one slot and `out` non-NULL the
+ * result is written directly.
+ */
+typedef struct ra_attn_args {
+  uint32_t struct_size;
+  int32_t q_dtype;                 /* RA_F16 or RA_BF16; also the dtype of out   */
+  const void* q;                   /* [total_q][num_q_heads][head_dim]           */
+  void* out;                       /* [total_q][num_q_heads][head_dim] or NULL   */
+  float* lse;                      /* [total_q][num_q_heads] or NULL             */
+  const void* k_cache;             /* paged layout above                         */
+  const void* v_cache;
+  int32_t kv_dtype;                /* RA_KV_*                                    */
+  float k_scale;                   /* (host) > 0, finite for E4M3 / INT8         */
+  float v_scale;
+  const int32_t* block_tables;     /* [batch][block_table_stride] page ids       */
+  int32_t block_table_stride;      /* entries >= ceil(ctx_b / 16) never read     */
+  const int32_t* context_lens;     /* [batch]                                    */
+  const int32_t* query_start_loc;  /* [batch + 1], non-decreasing, last = total_q*/
+  int32_t batch;
+  int32_t total_q;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;                /* 64 or 128                                  */
+  int32_t page_size;               /* 16                                         */
+  int64_t num_pages;               /* pages in each cache                        */
+  int32_t max_q_len;               /* (host) >= every q_len_b                    */
+  int32_t min_q_len;               /* (host) <= every q_len_b; 0 if unknown      */
+  int32_t max_context_len;         /* (host) >= every ctx_b, <= stride * 16      */
+  float softmax_scale;             /* > 0                                        */
+  int32_t window_left;             /* < 0: no window                             */
+  int32_t num_sinks;               /* >= 0; used only with a window              */
+  int32_t num_splits;              /* 0 = auto, 1..RA_KV_MAX_SPLITS              */
+  float* partial_out;              /* workspace, see above                       */
+  float* partial_lse;
+  int32_t partial_slots;           /* slots the partial buffers hold             */
+} ra_attn_args;
+
+/*
+ * ra_paged_attn -- decode/verify attention over the paged, quantised cache.
+ * Argument meaning, layouts and the split rule are given with ra_attn_args.
+ * Host checks: non-null pointers; 16-byte aligned q, out and caches;
+ * Hq % Hkv == 0; head_dim in {64, 128}; page_size == 16; known dtypes; finite
+ * positive scales for E4M3 / INT8; 1 <= max_q_len; max_context_len <=
+ * block_table_stride * 16; num_splits in [0, RA_KV_MAX_SPLITS]; partial
+ * buffers present and partial_slots >= the slots needed when more than one
+ * slot is used.
+ */
+int32_t ra_paged_attn(const ra_attn_args* args, void* stream);
+
+/*
+ * ra_paged_attn_workspace -- (host only, enqueues nothing) number of partition
+ * slots ra_paged_attn will use for these arguments, and the fp32 element counts
+ * of partial_out and partial_lse it needs (0 when one slot and out != NULL).
+ */
+int32_t ra_paged_attn_workspace(const ra_attn_args* args, int32_t* slots,
+                                int64_t* partial_out_floats,
+                                int64_t* partial_lse_floats);
+
+/*
+ * ra_lse_merge -- merge partial attention results by log-sum-exp.
+ *
+ * partial_out [num_partitions][rows][head_dim] fp32, partial_lse
+ * [num_partitions][rows] fp32 (natural log; -inf marks an empty partition,
+ * whose out is not read).  For each row: M = max_s lse_s; if M = -inf the
+ * result is out = 0, lse = -inf; else a_s = exp(lse_s - M),
+ * out = sum_s a_s out_s / sum_s a_s, lse = M + ln sum_s a_s, summed in the
+ * order s = 0, 1, ...  out [rows][head_dim] of out_dtype (RA_F16, RA_BF16 or
+ * RA_F32), lse_out [rows] fp32 or NULL.  head_dim in {64, 128};
+ * num_partitions in [1, RA_KV_MAX_SPLITS]; 16-byte aligned buffers.
+ * (ReVolta README, "Quick start" and "Hardware": decode context parallelism
+ * combines the partial attention of context parts.)
+ */
+int32_t ra_lse_merge(const float* partial_out, const float* partial_lse,
+                     int32_t num_partitions, int64_t rows, int32_t head_dim,
+                     void* out, int32_t out_dtype, float* lse_out, void* stream);
+
+/*
+ * ra_kv_gather_dequant -- (test and debugging aid) read one sequence's K or V
+ * back through its block-table row and dequantise it exactly.
+ * which: 0 = K cache, 1 = V cache.  out [ctx][num_kv_heads][head_dim] fp32 =
+ * fp32(decode(code)) * scale (FP16 caches: the fp16 value, scale ignored).
+ * Positions whose page id is outside [0, num_pages) are written as NaN.
+ */
+int32_t ra_kv_gather_dequant(const void* cache, int32_t which, int32_t kv_dtype,
+                             float scale, const int32_t* block_table_row,
+                             int32_t ctx, int64_t num_pages, int32_t num_kv_heads,
+                             int32_t head_dim, float* out, void* stream);
+
+/* Message describing the last non-OK status returned on this thread. */
+const char* ra_last_error(void);
+
+/* RA_KV_ABI_VERSION * 1000 + RA_KV_LAYOUT_ID. */
+int32_t ra_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RA_KV_H_ */

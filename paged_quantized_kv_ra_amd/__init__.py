@@ -7,7 +7,7 @@ at once (there is no fallback).
 """
 
 __all__ = ["kv_store", "paged_attn", "lse_merge", "kv_gather_dequant",
-           "paged_attn_workspace", "abi_version", "load_library"]
+           "paged_attn_workspace", "abi_version", "load_library", "new_cache", "RaError"]
 
 
 def __getattr__(name):

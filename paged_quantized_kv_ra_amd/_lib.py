@@ -1,0 +1,264 @@
+"""ctypes binding of libra_kv.so (C ABI in include/ra_kv.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  PyTorch provides device memory and the current stream.  torch is
+imported before the library is loaded so that libra_kv.so binds to the HIP
+runtime torch already mapped (one runtime per process).
+
+KV caches are torch tensors of shape [num_pages, num_kv_heads, 16 * head_dim]
+holding the library's paged layout: dtype float16 for FP16 caches, uint8 for
+E4M3 and INT8 codes.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libra_kv.so")
+
+RA_OK, RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED, RA_ERR_MISALIGNED, RA_ERR_WORKSPACE, RA_ERR_HIP = range(6)
+RA_F16, RA_BF16, RA_F32 = 1, 2, 3
+RA_KV_F16, RA_KV_FP8_E4M3, RA_KV_INT8 = 1, 2, 3
+KV_CODES = {"f16": RA_KV_F16, "e4m3": RA_KV_FP8_E4M3, "int8": RA_KV_INT8}
+PAGE = 16
+
+_c = ctypes
+_vp = _c.c_void_p
+
+
+class AttnArgs(_c.Structure):
+    """Mirror of ra_attn_args."""
+    _fields_ = [
+        ("struct_size", _c.c_uint32),
+        ("q_dtype", _c.c_int32),
+        ("q", _vp),
+        ("out", _vp),
+        ("lse", _vp),
+        ("k_cache", _vp),
+        ("v_cache", _vp),
+        ("kv_dtype", _c.c_int32),
+        ("k_scale", _c.c_float),
+        ("v_scale", _c.c_float),
+        ("block_tables", _vp),
+        ("block_table_stride", _c.c_int32),
+        ("context_lens", _vp),
+        ("query_start_loc", _vp),
+        ("batch", _c.c_int32),
+        ("total_q", _c.c_int32),
+        ("num_q_heads", _c.c_int32),
+        ("num_kv_heads", _c.c_int32),
+        ("head_dim", _c.c_int32),
+        ("page_size", _c.c_int32),
+        ("num_pages", _c.c_int64),
+        ("max_q_len", _c.c_int32),
+        ("min_q_len", _c.c_int32),
+        ("max_context_len", _c.c_int32),
+        ("softmax_scale", _c.c_float),
+        ("window_left", _c.c_int32),
+        ("num_sinks", _c.c_int32),
+        ("num_splits", _c.c_int32),
+        ("partial_out", _vp),
+        ("partial_lse", _vp),
+        ("partial_slots", _c.c_int32),
+    ]
+
+
+EXPORTED = {
+    "ra_kv_store": (_c.c_int32, [_vp, _vp, _c.c_int32, _c.c_int64, _c.c_int64, _vp, _c.c_int64, _vp, _vp,
+                                 _c.c_int32, _c.c_int64, _c.c_int32, _c.c_int32, _c.c_int32, _c.c_float,
+                                 _c.c_float, _vp]),
+    "ra_paged_attn": (_c.c_int32, [_c.POINTER(AttnArgs), _vp]),
+    "ra_paged_attn_workspace": (_c.c_int32, [_c.POINTER(AttnArgs), _c.POINTER(_c.c_int32),
+                                             _c.POINTER(_c.c_int64), _c.POINTER(_c.c_int64)]),
+    "ra_lse_merge": (_c.c_int32, [_vp, _vp, _c.c_int32, _c.c_int64, _c.c_int32, _vp, _c.c_int32, _vp, _vp]),
+    "ra_kv_gather_dequant": (_c.c_int32, [_vp, _c.c_int32, _c.c_int32, _c.c_float, _vp, _c.c_int32,
+                                          _c.c_int64, _c.c_int32, _c.c_int32, _vp, _vp]),
+    "ra_last_error": (_c.c_char_p, []),
+    "ra_abi_version": (_c.c_int32, []),
+}
+
+_LIB = None
+
+
+class RaError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"[status {status}] {msg}")
+        self.status = status
+
+
+def load_library():
+    """Load libra_kv.so (built in-tree); raise if it is missing."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m paged_quantized_kv_ra_amd.build`")
+        lib = _c.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTED.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = lib
+    return _LIB
+
+
+def _check(status):
+    if status != RA_OK:
+        raise RaError(status, load_library().ra_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else _vp(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return _vp(stream.cuda_stream)
+
+
+def abi_version():
+    return load_library().ra_abi_version()
+
+
+def _elem_bytes(kv_dtype):
+    return 2 if kv_dtype == "f16" else 1
+
+
+def new_cache(num_pages, num_kv_heads, head_dim, kv_dtype, device="cuda", fill=None):
+    """Allocate one K or V cache tensor in the library's layout."""
+    dt = torch.float16 if kv_dtype == "f16" else torch.uint8
+    t = torch.empty((num_pages, num_kv_heads, PAGE * head_dim), dtype=dt, device=device)
+    if fill is not None:
+        if kv_dtype == "f16":
+            t.view(torch.int16).fill_(fill if fill < 0x8000 else fill - 0x10000)
+        else:
+            t.fill_(fill)
+    return t
+
+
+def _src_code(t):
+    if t.dtype == torch.float16:
+        return RA_F16
+    if t.dtype == torch.bfloat16:
+        return RA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def kv_store(k, v, slot_mapping, k_cache, v_cache, kv_dtype, k_scale=1.0, v_scale=1.0, stream=None):
+    """Quantise k, v [T][Hkv][D] and scatter them into the caches at slot_mapping."""
+    T, hkv, D = k.shape
+    assert v.shape == k.shape and k.stride(2) == 1 and k.stride(1) == D and v.stride(2) == 1 and v.stride(1) == D
+    assert slot_mapping.dtype == torch.int64 and slot_mapping.numel() == T
+    num_pages = k_cache.shape[0]
+    _check(load_library().ra_kv_store(
+        _ptr(k), _ptr(v), _src_code(k), k.stride(0), v.stride(0), _ptr(slot_mapping), T,
+        _ptr(k_cache), _ptr(v_cache), KV_CODES[kv_dtype], num_pages, hkv, D, PAGE,
+        float(k_scale), float(v_scale), _stream(stream)))
+
+
+def _attn_args(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, kv_dtype, k_scale,
+               v_scale, softmax_scale, max_q_len, min_q_len, max_context_len, window_left, num_sinks,
+               num_splits, num_kv_heads):
+    T, hq, D = q.shape
+    a = AttnArgs()
+    a.struct_size = _c.sizeof(AttnArgs)
+    a.q_dtype = _src_code(q)
+    a.q = q.data_ptr()
+    a.k_cache = k_cache.data_ptr()
+    a.v_cache = v_cache.data_ptr()
+    a.kv_dtype = KV_CODES[kv_dtype]
+    a.k_scale = float(k_scale)
+    a.v_scale = float(v_scale)
+    a.block_tables = block_tables.data_ptr()
+    a.block_table_stride = block_tables.shape[1]
+    a.context_lens = context_lens.data_ptr()
+    a.query_start_loc = query_start_loc.data_ptr()
+    a.batch = context_lens.shape[0]
+    a.total_q = T
+    a.num_q_heads = hq
+    a.num_kv_heads = num_kv_heads
+    a.head_dim = D
+    a.page_size = PAGE
+    a.num_pages = k_cache.shape[0]
+    a.max_q_len = int(max_q_len)
+    a.min_q_len = int(min_q_len)
+    a.max_context_len = int(max_context_len)
+    a.softmax_scale = float(softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(D))
+    a.window_left = int(window_left)
+    a.num_sinks = int(num_sinks)
+    a.num_splits = int(num_splits)
+    return a
+
+
+def paged_attn_workspace(args):
+    slots = _c.c_int32()
+    po = _c.c_int64()
+    pl = _c.c_int64()
+    _check(load_library().ra_paged_attn_workspace(_c.byref(args), _c.byref(slots), _c.byref(po), _c.byref(pl)))
+    return slots.value, po.value, pl.value
+
+
+def paged_attn(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, *, kv_dtype,
+               max_q_len, max_context_len, k_scale=1.0, v_scale=1.0, softmax_scale=None, min_q_len=0,
+               window_left=-1, num_sinks=0, num_splits=0, out=None, lse=None, partials_only=False,
+               workspace=None, stream=None):
+    """Attention of the query blocks over the paged caches.
+
+    q [total_q][Hq][D] fp16/bf16; block_tables int32 [B][stride];
+    context_lens int32 [B]; query_start_loc int32 [B+1].  max_q_len and
+    max_context_len are host upper bounds.  Returns (out, lse), or with
+    partials_only=True (partial_out [S][total_q][Hq][D], partial_lse [S][total_q][Hq]).
+    """
+    T, hq, D = q.shape
+    hkv = k_cache.shape[1]
+    a = _attn_args(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, kv_dtype, k_scale,
+                   v_scale, softmax_scale, max_q_len, min_q_len, max_context_len, window_left, num_sinks,
+                   num_splits, hkv)
+    if not partials_only:
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty((T, hq), dtype=torch.float32, device=q.device)
+        a.out = out.data_ptr()
+        a.lse = lse.data_ptr()
+    slots, po_n, pl_n = paged_attn_workspace(a)
+    po = pl = None
+    if po_n > 0 or partials_only:
+        if workspace is not None:
+            po, pl = workspace
+        else:
+            po = torch.empty((slots, T, hq, D), dtype=torch.float32, device=q.device)
+            pl = torch.empty((slots, T, hq), dtype=torch.float32, device=q.device)
+        a.partial_out = po.data_ptr()
+        a.partial_lse = pl.data_ptr()
+        a.partial_slots = po.shape[0]
+    _check(load_library().ra_paged_attn(_c.byref(a), _stream(stream)))
+    if partials_only:
+        return po, pl
+    return out, lse
+
+
+def lse_merge(partial_out, partial_lse, out_dtype=torch.float32, out=None, lse=None, stream=None):
+    """Merge partials [S][rows...][D] / [S][rows...] into (out [rows...][D], lse [rows...])."""
+    S = partial_out.shape[0]
+    D = partial_out.shape[-1]
+    rows = partial_lse[0].numel()
+    code = {torch.float16: RA_F16, torch.bfloat16: RA_BF16, torch.float32: RA_F32}[out_dtype]
+    if out is None:
+        out = torch.empty(partial_out.shape[1:], dtype=out_dtype, device=partial_out.device)
+    if lse is None:
+        lse = torch.empty(partial_lse.shape[1:], dtype=torch.float32, device=partial_out.device)
+    _check(load_library().ra_lse_merge(_ptr(partial_out), _ptr(partial_lse), S, rows, D, _ptr(out), code,
+                                       _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+def kv_gather_dequant(cache, which, kv_dtype, scale, block_table_row, ctx, head_dim, stream=None):
+    """Exact dequantised [ctx][Hkv][D] fp32 read-back of one sequence's K (which=0) or V (1)."""
+    hkv = cache.shape[1]
+    out = torch.empty((ctx, hkv, head_dim), dtype=torch.float32, device=cache.device)
+    _check(load_library().ra_kv_gather_dequant(_ptr(cache), which, KV_CODES[kv_dtype], float(scale),
+                                               _ptr(block_table_row), ctx, cache.shape[0], hkv, head_dim,
+                                               _ptr(out), _stream(stream)))
+    return out

@@ -1,0 +1,190 @@
+// kv_store.hip -- quantise new K/V rows and scatter them into 16-token pages,
+// and the exact gather-dequantise read-back used to check the cache.
+//
+// The KV cache is written as FP16, FP8 E4M3 or INT8 with per-layer K and V
+// scales (ReVolta README, intro list and "Weight and KV formats"; "Running
+// FP4-Local on 4 x V100 32 GB (Volta) with ReVolta", "What it takes", for the
+// per-layer target K/V scale pack), into 16-token pages ("ReVolta 0.1.3",
+// "Known issues").
+//
+// One thread handles 8 consecutive dimensions of one (token, head): it reads
+// 16 bytes of K and 16 of V, quantises with a correctly rounded fp32 divide,
+// writes the K codes as one 8- or 16-byte store (a K row slice is contiguous
+// in the layout) and the V codes as single-element stores (V interleaves four
+// tokens per dimension).
+#include "ra_device.h"
+#include "ra_internal.h"
+
+namespace ra {
+namespace {
+
+template <int KV, int D, bool BF16>
+__global__ void __launch_bounds__(256) kv_store_kernel(StoreLaunch a) {
+  constexpr int E = KV == KV_F16 ? 2 : 1;
+  constexpr int CH = D / 8;                       // 8-dim chunks per head
+  const int64_t units = a.num_tokens * a.hkv * CH;
+  const int64_t limit = a.num_pages * kPage;
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < units;
+       u += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(u % CH);
+    const int64_t th = u / CH;
+    const int h = (int)(th % a.hkv);
+    const int64_t t = th / a.hkv;
+    const int64_t slot = a.slots[t];
+    if (slot < 0 || slot >= limit) continue;
+    const int64_t page = slot >> 4;
+    const int tp = (int)(slot & 15);
+    const int d0 = c * 8;
+
+    const uint16_t* ksrc = reinterpret_cast<const uint16_t*>(a.k) + t * a.k_stride + (int64_t)h * D + d0;
+    const uint16_t* vsrc = reinterpret_cast<const uint16_t*>(a.v) + t * a.v_stride + (int64_t)h * D + d0;
+    const u32x4 kr = load16(ksrc);
+    const u32x4 vr = load16(vsrc);
+    float kf[8], vf[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint16_t kb = (uint16_t)(kr[i >> 1] >> (16 * (i & 1)));
+      const uint16_t vb = (uint16_t)(vr[i >> 1] >> (16 * (i & 1)));
+      if constexpr (BF16) {
+        kf[i] = bf16_to_f32(kb);
+        vf[i] = bf16_to_f32(vb);
+      } else {
+        kf[i] = (float)as<f16>(kb);
+        vf[i] = (float)as<f16>(vb);
+      }
+    }
+    const int64_t blk = (page * a.hkv + h) * (int64_t)(kPage * D * E);
+    uint8_t* kc = reinterpret_cast<uint8_t*>(a.k_cache) + blk;
+    uint8_t* vc = reinterpret_cast<uint8_t*>(a.v_cache) + blk;
+
+    uint32_t kcode[8], vcode[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (KV == KV_F16) {
+        kcode[i] = as<uint16_t>((f16)kf[i]);
+        vcode[i] = as<uint16_t>((f16)vf[i]);
+      } else if constexpr (KV == KV_E4M3) {
+        kcode[i] = e4m3_encode(kf[i] / a.k_scale);
+        vcode[i] = e4m3_encode(vf[i] / a.v_scale);
+      } else {
+        kcode[i] = (uint32_t)i8_encode(kf[i] / a.k_scale) & 0xFFu;
+        vcode[i] = (uint32_t)i8_encode(vf[i] / a.v_scale) & 0xFFu;
+      }
+    }
+
+    // K: the 8 dims are contiguous inside one 16-byte piece of the layout.
+    const uint32_t koff = k_elem_offset<D, E>(tp, d0);
+    if constexpr (E == 2) {
+      u32x4 w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = kcode[2 * j] | (kcode[2 * j + 1] << 16);
+      *reinterpret_cast<u32x4*>(kc + koff) = w;
+    } else {
+      u32x2 w;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        w[j] = kcode[4 * j] | (kcode[4 * j + 1] << 8) | (kcode[4 * j + 2] << 16) | (kcode[4 * j + 3] << 24);
+      *reinterpret_cast<u32x2*>(kc + koff) = w;
+    }
+    // V: one element per store.
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t voff = v_elem_offset<D, E>(tp, d0 + i);
+      if constexpr (E == 2) *reinterpret_cast<uint16_t*>(vc + voff) = (uint16_t)vcode[i];
+      else vc[voff] = (uint8_t)vcode[i];
+    }
+  }
+}
+
+// out[j][h][d] = fp32(decode(code)) * scale, through the block-table row.
+template <int KV, int D, bool IS_V>
+__global__ void __launch_bounds__(256) kv_gather_kernel(GatherLaunch a) {
+  constexpr int E = KV == KV_F16 ? 2 : 1;
+  const int64_t n = (int64_t)a.ctx * a.hkv * (D / 4);   // 4 dims per thread
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < n;
+       u += (int64_t)gridDim.x * blockDim.x) {
+    const int d0 = (int)(u % (D / 4)) * 4;
+    const int64_t jh = u / (D / 4);
+    const int h = (int)(jh % a.hkv);
+    const int j = (int)(jh / a.hkv);
+    float* o = a.out + ((int64_t)j * a.hkv + h) * D + d0;
+    const int32_t page = a.bt_row[j >> 4];
+    if (page < 0 || page >= a.num_pages) {
+      for (int i = 0; i < 4; ++i) o[i] = __builtin_nanf("");
+      continue;
+    }
+    const int t = j & 15;
+    const uint8_t* blk = reinterpret_cast<const uint8_t*>(a.cache) +
+                         ((int64_t)page * a.hkv + h) * (int64_t)(kPage * D * E);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t off = IS_V ? v_elem_offset<D, E>(t, d0 + i) : k_elem_offset<D, E>(t, d0 + i);
+      float val;
+      if constexpr (KV == KV_F16) {
+        val = (float)as<f16>(*reinterpret_cast<const uint16_t*>(blk + off));
+      } else {
+        // decode through the same fp16 converters the attention kernels use
+        const f16x4 h4 = codes4_to_f16x4<KV>((uint32_t)blk[off]);
+        val = __fmul_rn((float)h4[0], a.scale);
+      }
+      o[i] = val;
+    }
+  }
+}
+
+template <int KV, int D>
+hipError_t store_dispatch_src(const StoreLaunch& a, hipStream_t s, dim3 g, dim3 b) {
+  if (a.src_bf16) hipLaunchKernelGGL((kv_store_kernel<KV, D, true>), g, b, 0, s, a);
+  else hipLaunchKernelGGL((kv_store_kernel<KV, D, false>), g, b, 0, s, a);
+  return hipGetLastError();
+}
+
+template <int KV>
+hipError_t store_dispatch_d(const StoreLaunch& a, hipStream_t s, dim3 g, dim3 b) {
+  return a.head_dim == 64 ? store_dispatch_src<KV, 64>(a, s, g, b)
+                          : store_dispatch_src<KV, 128>(a, s, g, b);
+}
+
+template <int KV, int D>
+hipError_t gather_dispatch_which(const GatherLaunch& a, hipStream_t s, dim3 g, dim3 b) {
+  if (a.which) hipLaunchKernelGGL((kv_gather_kernel<KV, D, true>), g, b, 0, s, a);
+  else hipLaunchKernelGGL((kv_gather_kernel<KV, D, false>), g, b, 0, s, a);
+  return hipGetLastError();
+}
+
+template <int KV>
+hipError_t gather_dispatch_d(const GatherLaunch& a, hipStream_t s, dim3 g, dim3 b) {
+  return a.head_dim == 64 ? gather_dispatch_which<KV, 64>(a, s, g, b)
+                          : gather_dispatch_which<KV, 128>(a, s, g, b);
+}
+
+dim3 grid_for(int64_t units) {
+  int64_t blocks = (units + 255) / 256;
+  if (blocks > 65536) blocks = 65536;   // grid-stride beyond this
+  if (blocks < 1) blocks = 1;
+  return dim3((unsigned)blocks);
+}
+
+}  // namespace
+
+hipError_t launch_kv_store(const StoreLaunch& a, hipStream_t s) {
+  if (a.num_tokens == 0) return hipSuccess;
+  const dim3 g = grid_for(a.num_tokens * a.hkv * (a.head_dim / 8)), b(256);
+  switch (a.kv) {
+    case KV_F16: return store_dispatch_d<KV_F16>(a, s, g, b);
+    case KV_E4M3: return store_dispatch_d<KV_E4M3>(a, s, g, b);
+    default: return store_dispatch_d<KV_I8>(a, s, g, b);
+  }
+}
+
+hipError_t launch_kv_gather(const GatherLaunch& a, hipStream_t s) {
+  if (a.ctx == 0) return hipSuccess;
+  const dim3 g = grid_for((int64_t)a.ctx * a.hkv * (a.head_dim / 4)), b(256);
+  switch (a.kv) {
+    case KV_F16: return gather_dispatch_d<KV_F16>(a, s, g, b);
+    case KV_E4M3: return gather_dispatch_d<KV_E4M3>(a, s, g, b);
+    default: return gather_dispatch_d<KV_I8>(a, s, g, b);
+  }
+}
+
+}  // namespace ra

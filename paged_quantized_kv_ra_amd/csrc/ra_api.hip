@@ -1,0 +1,311 @@
+// ra_api.hip -- the C ABI of libra_kv.so: host-side validation and dispatch.
+//
+// Every host-checkable precondition is checked before anything is enqueued
+// (the pages' engine rejects unsupported configurations before it loads
+// anything and refuses E4M3 KV without calibrated scales in strict mode:
+// ReVolta README, "Weight and KV formats"; "ReVolta 0.1.3", "Behaviour
+// changes").  On failure the call returns a status, records a message for
+// ra_last_error() and touches no output.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "ra_internal.h"
+#include "ra_kv.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool good_scale(float s) { return std::isfinite(s) && s > 0.0f; }
+
+int kv_kind(int32_t kv) {
+  switch (kv) {
+    case RA_KV_F16: return ra::KV_F16;
+    case RA_KV_FP8_E4M3: return ra::KV_E4M3;
+    case RA_KV_INT8: return ra::KV_I8;
+    default: return -1;
+  }
+}
+
+const char* kv_name(int32_t kv) {
+  return kv == RA_KV_F16 ? "FP16" : kv == RA_KV_FP8_E4M3 ? "FP8 E4M3" : "INT8";
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Split plan of an attention call: partition slots per sequence and, in the
+// automatic mode, each kernel's fixed partition size.
+struct Plan {
+  bool use_mfma, use_vec;
+  int32_t slots;
+  int32_t part_mfma, part_vec;
+  bool direct;
+};
+
+int32_t check_attn(const ra_attn_args* a, Plan* plan) {
+  if (!a) return fail(RA_ERR_INVALID_ARG, "ra_paged_attn: args is NULL");
+  if (a->struct_size < sizeof(ra_attn_args))
+    return fail(RA_ERR_INVALID_ARG, "ra_paged_attn: struct_size %u < %zu (ABI %d)", a->struct_size,
+                sizeof(ra_attn_args), RA_KV_ABI_VERSION);
+  if (a->batch < 0 || a->total_q < 0)
+    return fail(RA_ERR_INVALID_ARG, "ra_paged_attn: batch (%d) and total_q (%d) must be >= 0", a->batch,
+                a->total_q);
+  if (a->q_dtype != RA_F16 && a->q_dtype != RA_BF16)
+    return fail(RA_ERR_UNSUPPORTED, "ra_paged_attn: q_dtype %d is not RA_F16 or RA_BF16", a->q_dtype);
+  if (kv_kind(a->kv_dtype) < 0)
+    return fail(RA_ERR_UNSUPPORTED, "ra_paged_attn: unknown kv_dtype %d", a->kv_dtype);
+  if (a->head_dim != 64 && a->head_dim != 128)
+    return fail(RA_ERR_UNSUPPORTED, "ra_paged_attn: head_dim %d is not 64 or 128", a->head_dim);
+  if (a->page_size != RA_KV_PAGE_SIZE)
+    return fail(RA_ERR_UNSUPPORTED, "ra_paged_attn: page_size %d is not 16", a->page_size);
+  if (a->num_q_heads < 1 || a->num_kv_heads < 1 || a->num_q_heads % a->num_kv_heads != 0)
+    return fail(RA_ERR_INVALID_ARG, "ra_paged_attn: num_q_heads %d must be a positive multiple of num_kv_heads %d",
+                a->num_q_heads, a->num_kv_heads);
+  if (a->num_pages < 1) return fail(RA_ERR_INVALID_ARG, "ra_paged_attn: num_pages must be >= 1");
+  if (a->block_table_stride < 1) return fail(RA_ERR_INVALID_ARG, "ra_paged_attn: block_table_stride must be >= 1");
+  if (a->max_q_len < 1) return fail(RA_ERR_INVALID_ARG, "ra_paged_attn: max_q_len must be >= 1");
+  if (a->min_q_len < 0 || a->min_q_len > a->max_q_len)
+    return fail(RA_ERR_INVALID_ARG, "ra_paged_attn: min_q_len %d outside [0, max_q_len %d]", a->min_q_len,
+                a->max_q_len);
+  if (a->max_context_len < 0 || (int64_t)a->max_context_len > (int64_t)a->block_table_stride * RA_KV_PAGE_SIZE)
+    return fail(RA_ERR_INVALID_ARG, "ra_paged_attn: max_context_len %d outside [0, block_table_stride * 16 = %lld]",
+                a->max_context_len, (long long)a->block_table_stride * RA_KV_PAGE_SIZE);
+  if (!(std::isfinite(a->softmax_scale) && a->softmax_scale > 0.0f))
+    return fail(RA_ERR_INVALID_ARG, "ra_paged_attn: softmax_scale must be finite and > 0");
+  if (a->kv_dtype != RA_KV_F16 && !(good_scale(a->k_scale) && good_scale(a->v_scale)))
+    return fail(RA_ERR_INVALID_ARG,
+                "ra_paged_attn: %s KV needs finite positive per-layer k_scale and v_scale (got %g, %g); "
+                "there is no fallback scale", kv_name(a->kv_dtype), (double)a->k_scale, (double)a->v_scale);
+  if (a->num_sinks < 0) return fail(RA_ERR_INVALID_ARG, "ra_paged_attn: num_sinks must be >= 0");
+  if (a->num_splits < 0 || a->num_splits > RA_KV_MAX_SPLITS)
+    return fail(RA_ERR_INVALID_ARG, "ra_paged_attn: num_splits %d outside [0, %d]", a->num_splits,
+                RA_KV_MAX_SPLITS);
+
+  const int64_t g = a->num_q_heads / a->num_kv_heads;
+  const int64_t rows_max = g * a->max_q_len;
+  const int64_t rows_min = g * (a->min_q_len > 0 ? a->min_q_len : 1);
+  plan->use_mfma = rows_max >= ra::kMfmaMinRows;
+  plan->use_vec = rows_min < ra::kMfmaMinRows;
+  plan->part_mfma = ra::kAutoPartMfma;
+  plan->part_vec = ra::kAutoPartVec;
+  if (a->num_splits > 0) {
+    plan->slots = a->num_splits;
+  } else {
+    int64_t s = 1;
+    if (plan->use_mfma) s = std::max<int64_t>(s, ceil_div(a->max_context_len, plan->part_mfma));
+    if (plan->use_vec) s = std::max<int64_t>(s, ceil_div(a->max_context_len, plan->part_vec));
+    if (s > RA_KV_MAX_SPLITS * 64)
+      return fail(RA_ERR_INVALID_ARG, "ra_paged_attn: max_context_len %d needs too many partitions",
+                  a->max_context_len);
+    plan->slots = (int32_t)s;
+  }
+  plan->direct = plan->slots == 1 && a->out != nullptr;
+
+  // grid size: slots * Hkv * row groups * batch blocks
+  const int64_t rg = std::max<int64_t>(ceil_div(rows_max, ra::kMfmaRowsPerBlock),
+                                       ceil_div(std::min<int64_t>(rows_max, ra::kMfmaMinRows - 1),
+                                                ra::kVecRowsPerBlock));
+  if ((int64_t)plan->slots * a->num_kv_heads * rg * a->batch > (int64_t)0x7FFFFFF0)
+    return fail(RA_ERR_INVALID_ARG, "ra_paged_attn: problem needs more than 2^31 workgroups");
+  return RA_OK;
+}
+
+int32_t check_attn_pointers(const ra_attn_args* a, const Plan& p) {
+  if (!a->q || !a->k_cache || !a->v_cache || !a->block_tables || !a->context_lens || !a->query_start_loc)
+    return fail(RA_ERR_INVALID_ARG,
+                "ra_paged_attn: q, k_cache, v_cache, block_tables, context_lens and query_start_loc must be non-NULL");
+  if (!aligned16(a->q) || !aligned16(a->k_cache) || !aligned16(a->v_cache) || (a->out && !aligned16(a->out)))
+    return fail(RA_ERR_MISALIGNED, "ra_paged_attn: q, out, k_cache and v_cache must be 16-byte aligned");
+  if (!p.direct) {
+    if (!a->partial_out || !a->partial_lse)
+      return fail(RA_ERR_WORKSPACE, "ra_paged_attn: %d partition slot(s) need partial_out and partial_lse%s",
+                  p.slots, a->out ? "" : " (out is NULL)");
+    if (a->partial_slots < p.slots)
+      return fail(RA_ERR_WORKSPACE, "ra_paged_attn: partial buffers hold %d slots, %d needed", a->partial_slots,
+                  p.slots);
+    if (!aligned16(a->partial_out))
+      return fail(RA_ERR_MISALIGNED, "ra_paged_attn: partial_out must be 16-byte aligned");
+  }
+  return RA_OK;
+}
+
+ra::AttnLaunch make_launch(const ra_attn_args* a, const Plan& p) {
+  ra::AttnLaunch L{};
+  L.q = a->q;
+  L.q_bf16 = a->q_dtype == RA_BF16;
+  L.out = p.direct ? a->out : nullptr;
+  L.lse = p.direct ? a->lse : nullptr;
+  L.part_out = a->partial_out;
+  L.part_lse = a->partial_lse;
+  L.k_cache = static_cast<const uint8_t*>(a->k_cache);
+  L.v_cache = static_cast<const uint8_t*>(a->v_cache);
+  L.kv = kv_kind(a->kv_dtype);
+  const bool quant = a->kv_dtype != RA_KV_F16;
+  L.k_scale = quant ? a->k_scale : 1.0f;
+  L.v_scale = quant ? a->v_scale : 1.0f;
+  L.block_tables = a->block_tables;
+  L.bt_stride = a->block_table_stride;
+  L.context_lens = a->context_lens;
+  L.qsl = a->query_start_loc;
+  L.batch = a->batch;
+  L.total_q = a->total_q;
+  L.hq = a->num_q_heads;
+  L.hkv = a->num_kv_heads;
+  L.head_dim = a->head_dim;
+  L.num_pages = a->num_pages;
+  L.max_q_len = a->max_q_len;
+  L.max_ctx = a->max_context_len;
+  L.softmax_scale = a->softmax_scale;
+  L.window = a->window_left < 0 ? -1 : a->window_left;
+  L.sinks = a->window_left < 0 ? 0 : a->num_sinks;
+  L.num_splits = a->num_splits;
+  L.slots = p.slots;
+  L.direct = p.direct;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ra_kv_store(const void* k, const void* v, int32_t src_dtype, int64_t k_token_stride,
+                    int64_t v_token_stride, const int64_t* slot_mapping, int64_t num_tokens, void* k_cache,
+                    void* v_cache, int32_t kv_dtype, int64_t num_pages, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t page_size, float k_scale, float v_scale, void* stream) {
+  if (num_tokens < 0) return fail(RA_ERR_INVALID_ARG, "ra_kv_store: num_tokens must be >= 0");
+  if (src_dtype != RA_F16 && src_dtype != RA_BF16)
+    return fail(RA_ERR_UNSUPPORTED, "ra_kv_store: src_dtype %d is not RA_F16 or RA_BF16", src_dtype);
+  if (kv_kind(kv_dtype) < 0) return fail(RA_ERR_UNSUPPORTED, "ra_kv_store: unknown kv_dtype %d", kv_dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(RA_ERR_UNSUPPORTED, "ra_kv_store: head_dim %d is not 64 or 128", head_dim);
+  if (page_size != RA_KV_PAGE_SIZE)
+    return fail(RA_ERR_UNSUPPORTED, "ra_kv_store: page_size %d is not 16", page_size);
+  if (num_kv_heads < 1) return fail(RA_ERR_INVALID_ARG, "ra_kv_store: num_kv_heads must be >= 1");
+  if (num_pages < 1) return fail(RA_ERR_INVALID_ARG, "ra_kv_store: num_pages must be >= 1");
+  if (kv_dtype != RA_KV_F16 && !(good_scale(k_scale) && good_scale(v_scale)))
+    return fail(RA_ERR_INVALID_ARG,
+                "ra_kv_store: %s KV needs finite positive per-layer k_scale and v_scale (got %g, %g); "
+                "there is no fallback scale", kv_name(kv_dtype), (double)k_scale, (double)v_scale);
+  if (k_token_stride < (int64_t)num_kv_heads * head_dim || v_token_stride < (int64_t)num_kv_heads * head_dim)
+    return fail(RA_ERR_INVALID_ARG, "ra_kv_store: token strides (%lld, %lld) smaller than num_kv_heads * head_dim",
+                (long long)k_token_stride, (long long)v_token_stride);
+  if (num_tokens == 0) return RA_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache)
+    return fail(RA_ERR_INVALID_ARG, "ra_kv_store: k, v, slot_mapping, k_cache and v_cache must be non-NULL");
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache) || (k_token_stride % 8) ||
+      (v_token_stride % 8))
+    return fail(RA_ERR_MISALIGNED,
+                "ra_kv_store: k, v, k_cache, v_cache must be 16-byte aligned and token strides multiples of 8");
+  ra::StoreLaunch L{k, v, src_dtype == RA_BF16, k_token_stride, v_token_stride, slot_mapping, num_tokens,
+                    k_cache, v_cache, kv_kind(kv_dtype), num_pages, num_kv_heads, head_dim,
+                    kv_dtype == RA_KV_F16 ? 1.0f : k_scale, kv_dtype == RA_KV_F16 ? 1.0f : v_scale};
+  const hipError_t e = ra::launch_kv_store(L, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(RA_ERR_HIP, "ra_kv_store: launch failed: %s", hipGetErrorString(e));
+  return RA_OK;
+}
+
+int32_t ra_paged_attn_workspace(const ra_attn_args* args, int32_t* slots, int64_t* partial_out_floats,
+                                int64_t* partial_lse_floats) {
+  Plan p{};
+  const int32_t st = check_attn(args, &p);
+  if (st != RA_OK) return st;
+  const int64_t rows = (int64_t)args->total_q * args->num_q_heads;
+  if (slots) *slots = p.slots;
+  if (partial_out_floats) *partial_out_floats = p.direct ? 0 : (int64_t)p.slots * rows * args->head_dim;
+  if (partial_lse_floats) *partial_lse_floats = p.direct ? 0 : (int64_t)p.slots * rows;
+  return RA_OK;
+}
+
+int32_t ra_paged_attn(const ra_attn_args* args, void* stream) {
+  Plan p{};
+  int32_t st = check_attn(args, &p);
+  if (st != RA_OK) return st;
+  if (args->batch == 0 || args->total_q == 0) return RA_OK;
+  st = check_attn_pointers(args, p);
+  if (st != RA_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  ra::AttnLaunch L = make_launch(args, p);
+  hipError_t e = hipSuccess;
+  if (p.use_mfma) {
+    L.part_tokens = p.part_mfma;
+    e = ra::launch_attn_mfma(L, s);
+    if (e != hipSuccess) return fail(RA_ERR_HIP, "ra_paged_attn: matrix-core kernel launch failed: %s", hipGetErrorString(e));
+  }
+  if (p.use_vec) {
+    L.part_tokens = p.part_vec;
+    e = ra::launch_attn_vec(L, s);
+    if (e != hipSuccess) return fail(RA_ERR_HIP, "ra_paged_attn: vector kernel launch failed: %s", hipGetErrorString(e));
+  }
+  if (!p.direct && args->out) {
+    ra::MergeLaunch M{args->partial_out, args->partial_lse, p.slots, (int64_t)args->total_q * args->num_q_heads,
+                      args->head_dim, args->out, args->q_dtype, args->lse};
+    e = ra::launch_lse_merge(M, s);
+    if (e != hipSuccess) return fail(RA_ERR_HIP, "ra_paged_attn: merge launch failed: %s", hipGetErrorString(e));
+  }
+  return RA_OK;
+}
+
+int32_t ra_lse_merge(const float* partial_out, const float* partial_lse, int32_t num_partitions, int64_t rows,
+                     int32_t head_dim, void* out, int32_t out_dtype, float* lse_out, void* stream) {
+  if (num_partitions < 1 || num_partitions > RA_KV_MAX_SPLITS)
+    return fail(RA_ERR_INVALID_ARG, "ra_lse_merge: num_partitions %d outside [1, %d]", num_partitions,
+                RA_KV_MAX_SPLITS);
+  if (rows < 0) return fail(RA_ERR_INVALID_ARG, "ra_lse_merge: rows must be >= 0");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(RA_ERR_UNSUPPORTED, "ra_lse_merge: head_dim %d is not 64 or 128", head_dim);
+  if (out_dtype != RA_F16 && out_dtype != RA_BF16 && out_dtype != RA_F32)
+    return fail(RA_ERR_UNSUPPORTED, "ra_lse_merge: out_dtype %d unknown", out_dtype);
+  if (rows == 0) return RA_OK;
+  if (rows > (int64_t)0x7FFFFFF0 * 4) return fail(RA_ERR_INVALID_ARG, "ra_lse_merge: too many rows");
+  if (!partial_out || !partial_lse || !out)
+    return fail(RA_ERR_INVALID_ARG, "ra_lse_merge: partial_out, partial_lse and out must be non-NULL");
+  if (!aligned16(partial_out) || !aligned16(out))
+    return fail(RA_ERR_MISALIGNED, "ra_lse_merge: partial_out and out must be 16-byte aligned");
+  ra::MergeLaunch M{partial_out, partial_lse, num_partitions, rows, head_dim, out, out_dtype, lse_out};
+  const hipError_t e = ra::launch_lse_merge(M, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(RA_ERR_HIP, "ra_lse_merge: launch failed: %s", hipGetErrorString(e));
+  return RA_OK;
+}
+
+int32_t ra_kv_gather_dequant(const void* cache, int32_t which, int32_t kv_dtype, float scale,
+                             const int32_t* block_table_row, int32_t ctx, int64_t num_pages, int32_t num_kv_heads,
+                             int32_t head_dim, float* out, void* stream) {
+  if (which != 0 && which != 1) return fail(RA_ERR_INVALID_ARG, "ra_kv_gather_dequant: which must be 0 (K) or 1 (V)");
+  if (kv_kind(kv_dtype) < 0) return fail(RA_ERR_UNSUPPORTED, "ra_kv_gather_dequant: unknown kv_dtype %d", kv_dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(RA_ERR_UNSUPPORTED, "ra_kv_gather_dequant: head_dim %d is not 64 or 128", head_dim);
+  if (ctx < 0 || num_pages < 1 || num_kv_heads < 1)
+    return fail(RA_ERR_INVALID_ARG, "ra_kv_gather_dequant: ctx >= 0, num_pages >= 1 and num_kv_heads >= 1 required");
+  if (kv_dtype != RA_KV_F16 && !good_scale(scale))
+    return fail(RA_ERR_INVALID_ARG, "ra_kv_gather_dequant: scale must be finite and > 0");
+  if (ctx == 0) return RA_OK;
+  if (!cache || !block_table_row || !out)
+    return fail(RA_ERR_INVALID_ARG, "ra_kv_gather_dequant: cache, block_table_row and out must be non-NULL");
+  if (!aligned16(cache)) return fail(RA_ERR_MISALIGNED, "ra_kv_gather_dequant: cache must be 16-byte aligned");
+  ra::GatherLaunch G{cache, which, kv_kind(kv_dtype), kv_dtype == RA_KV_F16 ? 1.0f : scale, block_table_row, ctx,
+                     num_pages, num_kv_heads, head_dim, out};
+  const hipError_t e = ra::launch_kv_gather(G, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(RA_ERR_HIP, "ra_kv_gather_dequant: launch failed: %s", hipGetErrorString(e));
+  return RA_OK;
+}
+
+const char* ra_last_error(void) { return g_err.c_str(); }
+
+int32_t ra_abi_version(void) { return RA_KV_ABI_VERSION * 1000 + RA_KV_LAYOUT_ID; }
+
+}  // extern "C"

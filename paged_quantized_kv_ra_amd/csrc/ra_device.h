@@ -1,0 +1,142 @@
+// ra_device.h -- device-side types and helpers shared by the gfx950 kernels.
+//
+// KV element formats (ReVolta README, intro list and "Weight and KV formats"):
+// FP16, FP8 E4M3 (OCP E4M3FN) and INT8, with per-layer scalar scales; the
+// arithmetic runs on FP16 operands converted exactly from the stored codes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ra_internal.h"
+
+namespace ra {
+
+typedef _Float16 f16;
+typedef f16 f16x2 __attribute__((ext_vector_type(2)));
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kPage = 16;
+constexpr int kWave = 64;
+
+// Bit reinterpretation through a by-value copy.  (hipcc's __builtin_bit_cast
+// applied directly to a vector-element subscript such as v[i] reads element 0;
+// passing the value through a parameter sidesteps that.)
+template <class To, class From>
+__device__ __forceinline__ To as(From x) {
+  static_assert(sizeof(To) == sizeof(From), "size mismatch");
+  return __builtin_bit_cast(To, x);
+}
+
+// ---------------------------------------------------------------------------
+// Encoders (the store's quantiser).  Bit-level, independent of any table.
+
+// fp32 -> OCP E4M3 byte: saturate to +-448, round to nearest even, keep the
+// sign, NaN -> 0x7F | sign.
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return 0x7Fu | sign;            // NaN
+  const float af = __uint_as_float(a);
+  uint32_t mag;
+  if (af >= 448.0f) {
+    mag = 0x7Eu;                                       // saturate (inf too)
+  } else if (af < 0.015625f) {                         // below 2^-6: steps of 2^-9
+    mag = (uint32_t)__builtin_rintf(af * 512.0f);      // exact scaling, RNE; 8 = 2^-6
+  } else {
+    // keep 3 mantissa bits: round the low 20 bits to nearest even
+    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    mag = (r >> 20) - (120u << 3);                     // rebias exponent 127 -> 7
+  }
+  return mag | sign;
+}
+
+// fp32 -> int8 code: round half to even, clamp to [-127, 127], NaN -> 0.
+__device__ __forceinline__ int32_t i8_encode(float y) {
+  if (!(y == y)) return 0;
+  float r = __builtin_rintf(y);
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return (int32_t)r;
+}
+
+// ---------------------------------------------------------------------------
+// Exact decoders to FP16 operands.
+
+// Four E4M3 bytes (little-endian in x) -> four fp16 values, exactly (every
+// E4M3 value, subnormals included, is an fp16 value).  The gfx950 scaled
+// conversion with scale 1.0 is exact.
+__device__ __forceinline__ f16x4 e4m3x4_to_f16x4(uint32_t x) {
+  const f16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, false);
+  const f16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, true);
+  return f16x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// Four int8 bytes -> four fp16 values, exactly: 0x6400 | (b ^ 0x80) is the
+// fp16 number 1024 + (b + 128); subtracting 1152 leaves b.
+__device__ __forceinline__ f16x4 i8x4_to_f16x4(uint32_t x) {
+  const uint32_t ux = x ^ 0x80808080u;
+  const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, ux, 0x04010400u);  // [b1' 64 b0' 64]
+  const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, ux, 0x04030402u);  // [b3' 64 b2' 64]
+  f16x2 l = as<f16x2>(lo);
+  f16x2 h = as<f16x2>(hi);
+  const f16x2 off = {(f16)1152.0f, (f16)1152.0f};
+  l = l - off;
+  h = h - off;
+  return f16x4{l[0], l[1], h[0], h[1]};
+}
+
+template <int KV>
+__device__ __forceinline__ f16x4 codes4_to_f16x4(uint32_t x) {
+  if constexpr (KV == KV_E4M3) return e4m3x4_to_f16x4(x);
+  else return i8x4_to_f16x4(x);
+}
+
+// bf16 bit pattern -> fp32 (exact)
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// fp32 -> bf16 bit pattern, round to nearest even (NaN kept quiet)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// Paged layout: byte offsets of an element inside its (page, head) block.
+
+template <int D, int E>
+__device__ __forceinline__ uint32_t k_elem_offset(int t, int d) {
+  constexpr int Q = D / 4;
+  const int lane = 16 * (d / Q) + t;
+  const int b = (d % Q) * E;
+  return (uint32_t)((b >> 4) * 1024 + lane * 16 + (b & 15));
+}
+
+template <int D, int E>
+__device__ __forceinline__ uint32_t v_elem_offset(int t, int d) {
+  constexpr int W = D / 16;
+  const int lane = 16 * (t / 4) + d / W;
+  const int b = ((d % W) * 4 + (t % 4)) * E;
+  return (uint32_t)((b >> 4) * 1024 + lane * 16 + (b & 15));
+}
+
+// ---------------------------------------------------------------------------
+// 16-byte global load (one lane's piece of a 1 KiB wavefront slab).
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+}  // namespace ra

@@ -1,0 +1,106 @@
+// ra_internal.h -- host-side launch interface between the C ABI layer
+// (ra_api.hip, which validates arguments) and the kernel translation units.
+// Launchers assume validated arguments and return the HIP launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ra {
+
+enum KvKind { KV_F16 = 0, KV_E4M3 = 1, KV_I8 = 2 };
+
+struct StoreLaunch {
+  const void* k;
+  const void* v;
+  bool src_bf16;
+  int64_t k_stride;      // elements
+  int64_t v_stride;
+  const int64_t* slots;
+  int64_t num_tokens;
+  void* k_cache;
+  void* v_cache;
+  int kv;                // KvKind
+  int64_t num_pages;
+  int hkv;
+  int head_dim;
+  float k_scale;
+  float v_scale;
+};
+hipError_t launch_kv_store(const StoreLaunch& a, hipStream_t s);
+
+struct GatherLaunch {
+  const void* cache;
+  int which;             // 0 K, 1 V
+  int kv;
+  float scale;
+  const int32_t* bt_row;
+  int32_t ctx;
+  int64_t num_pages;
+  int hkv;
+  int head_dim;
+  float* out;
+};
+hipError_t launch_kv_gather(const GatherLaunch& a, hipStream_t s);
+
+// Attention work description shared by both attention kernels.
+struct AttnLaunch {
+  const void* q;
+  bool q_bf16;
+  void* out;             // final output (direct write) or nullptr
+  float* lse;            // final lse (direct write) or nullptr
+  float* part_out;       // [slots][total_q][Hq][D] when slots > 1 or out == nullptr
+  float* part_lse;       // [slots][total_q][Hq]
+  const uint8_t* k_cache;
+  const uint8_t* v_cache;
+  int kv;                // KvKind
+  float k_scale;         // 1 for FP16 caches
+  float v_scale;
+  const int32_t* block_tables;
+  int32_t bt_stride;
+  const int32_t* context_lens;
+  const int32_t* qsl;
+  int32_t batch;
+  int32_t total_q;
+  int32_t hq;
+  int32_t hkv;
+  int32_t head_dim;
+  int64_t num_pages;
+  int32_t max_q_len;
+  int32_t max_ctx;
+  float softmax_scale;
+  int32_t window;        // < 0: none
+  int32_t sinks;
+  int32_t num_splits;    // > 0 explicit, 0 auto
+  int32_t slots;         // partition slots per sequence in the grid
+  int32_t part_tokens;   // auto mode: fixed partition size in tokens
+  bool direct;           // write out/lse directly (one slot)
+};
+
+// Rows of a (sequence, KV head) unit: g * q_len.  Sequences with
+// g * q_len >= kMfmaMinRows use the matrix-core kernel, the rest the
+// vector kernel.
+constexpr int kMfmaMinRows = 16;
+constexpr int kMfmaRowsPerBlock = 48;   // rows beyond this split over row groups
+constexpr int kVecRowsPerBlock = 8;
+
+// Automatic partition sizes (tokens), constants of the library.
+constexpr int kAutoPartMfma = 2048;
+constexpr int kAutoPartVec = 1024;
+
+hipError_t launch_attn_mfma(const AttnLaunch& a, hipStream_t s);
+hipError_t launch_attn_vec(const AttnLaunch& a, hipStream_t s);
+
+struct MergeLaunch {
+  const float* part_out;
+  const float* part_lse;
+  int32_t parts;
+  int64_t rows;
+  int32_t head_dim;
+  void* out;
+  int out_dtype;         // 1 f16, 2 bf16, 3 f32
+  float* lse;
+};
+hipError_t launch_lse_merge(const MergeLaunch& a, hipStream_t s);
+
+}  // namespace ra

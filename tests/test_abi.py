@@ -1,0 +1,256 @@
+"""C ABI checks that run without a GPU.
+
+* libra_kv.so loads and exports every function include/ra_kv.h declares;
+* the ctypes mirror of ra_attn_args has the C layout (sizeof / offsetof from
+  a C program compiled against the header with gcc);
+* every host-side validation path returns its status and message before any
+  HIP call (fake, never-dereferenced pointers are passed).
+"""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "ra_kv.h")
+
+
+def _lib():
+    from paged_quantized_kv_ra_amd import _lib as L
+    if not os.path.exists(L.LIB_PATH):
+        pytest.skip("libra_kv.so not built")
+    return L
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ra_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    L = _lib()
+    lib = L.load_library()
+    names = declared_functions()
+    assert len(names) >= 7
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in L.EXPORTED, f"{n} has no ctypes prototype"
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}$", out, re.M), n
+
+
+def test_abi_version():
+    L = _lib()
+    assert L.abi_version() == 1001
+
+
+def test_struct_layout_matches_c():
+    L = _lib()
+    fields = [f for f, _ in L.AttnArgs._fields_]
+    src = ['#include <stdio.h>', '#include <stddef.h>', '#include "ra_kv.h"', 'int main(void) {',
+           'printf("size %zu\\n", sizeof(ra_attn_args));']
+    src += [f'printf("{f} %zu\\n", offsetof(ra_attn_args, {f}));' for f in fields]
+    src += ["return 0; }"]
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "t.c")
+        open(c, "w").write("\n".join(src))
+        exe = os.path.join(d, "t")
+        subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), c, "-o", exe],
+                       check=True)
+        got = dict(l.split() for l in subprocess.run([exe], capture_output=True, text=True).stdout.splitlines())
+    assert int(got["size"]) == ctypes.sizeof(L.AttnArgs)
+    for f in fields:
+        assert int(got[f]) == getattr(L.AttnArgs, f).offset, f
+
+
+def test_header_compiles_as_c_and_cpp():
+    with tempfile.TemporaryDirectory() as d:
+        for comp, ext in (("gcc", "c"), ("g++", "cpp")):
+            p = os.path.join(d, "h." + ext)
+            open(p, "w").write("#include \"ra_kv.h\"\nint32_t (*f)(void) = ra_abi_version;\nint main(void){return f == 0;}\n")
+            subprocess.run([comp, "-Wall", "-Werror", "-Wno-address", "-c", "-I", os.path.dirname(HEADER), p, "-o",
+                            os.path.join(d, "h.o")], check=True)
+
+
+FAKE = 0x100000      # 16-byte aligned, never dereferenced by validation
+
+
+def _good_args(L, **kw):
+    a = L.AttnArgs()
+    a.struct_size = ctypes.sizeof(L.AttnArgs)
+    a.q_dtype = L.RA_F16
+    a.q = FAKE
+    a.out = FAKE
+    a.lse = FAKE
+    a.k_cache = FAKE
+    a.v_cache = FAKE
+    a.kv_dtype = L.RA_KV_FP8_E4M3
+    a.k_scale = 0.01
+    a.v_scale = 0.01
+    a.block_tables = FAKE
+    a.block_table_stride = 4
+    a.context_lens = FAKE
+    a.query_start_loc = FAKE
+    a.batch = 2
+    a.total_q = 10
+    a.num_q_heads = 16
+    a.num_kv_heads = 2
+    a.head_dim = 128
+    a.page_size = 16
+    a.num_pages = 100
+    a.max_q_len = 5
+    a.min_q_len = 5
+    a.max_context_len = 64
+    a.softmax_scale = 0.088
+    a.window_left = -1
+    a.num_sinks = 0
+    a.num_splits = 1
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+BAD_ATTN = [
+    (dict(struct_size=8), 1, "struct_size"),
+    (dict(batch=-1), 1, "batch"),
+    (dict(q_dtype=3), 2, "q_dtype"),
+    (dict(kv_dtype=9), 2, "kv_dtype"),
+    (dict(head_dim=96), 2, "head_dim"),
+    (dict(page_size=32), 2, "page_size"),
+    (dict(num_q_heads=15), 1, "multiple"),
+    (dict(num_kv_heads=0), 1, "multiple"),
+    (dict(num_pages=0), 1, "num_pages"),
+    (dict(block_table_stride=0), 1, "block_table_stride"),
+    (dict(max_q_len=0), 1, "max_q_len"),
+    (dict(min_q_len=6), 1, "min_q_len"),
+    (dict(max_context_len=65), 1, "max_context_len"),
+    (dict(softmax_scale=0.0), 1, "softmax_scale"),
+    (dict(softmax_scale=float("nan")), 1, "softmax_scale"),
+    (dict(k_scale=0.0), 1, "no fallback"),
+    (dict(v_scale=float("inf")), 1, "no fallback"),
+    (dict(k_scale=-1.0), 1, "no fallback"),
+    (dict(kv_dtype=3, v_scale=float("nan")), 1, "INT8"),
+    (dict(num_sinks=-1), 1, "num_sinks"),
+    (dict(num_splits=-1), 1, "num_splits"),
+    (dict(num_splits=5000), 1, "num_splits"),
+    (dict(q=0), 1, "non-NULL"),
+    (dict(block_tables=0), 1, "non-NULL"),
+    (dict(q=FAKE + 8), 3, "aligned"),
+    (dict(k_cache=FAKE + 4), 3, "aligned"),
+    (dict(out=FAKE + 2), 3, "aligned"),
+    (dict(num_splits=4), 4, "partial_out"),
+    (dict(num_splits=4, partial_out=FAKE, partial_lse=FAKE, partial_slots=3), 4, "slots"),
+    (dict(num_splits=4, partial_out=FAKE + 4, partial_lse=FAKE, partial_slots=4), 3, "partial_out"),
+    (dict(out=0, num_splits=1), 4, "out is NULL"),
+]
+
+
+@pytest.mark.parametrize("kw,status,msg", BAD_ATTN)
+def test_attn_validation(kw, status, msg):
+    L = _lib()
+    lib = L.load_library()
+    a = _good_args(L, **kw)
+    st = lib.ra_paged_attn(ctypes.byref(a), None)
+    assert st == status, (st, lib.ra_last_error())
+    assert msg in lib.ra_last_error().decode()
+
+
+def test_fp16_cache_ignores_scales_and_workspace_query():
+    L = _lib()
+    a = _good_args(L, kv_dtype=1, k_scale=0.0, v_scale=float("nan"), num_splits=0, max_context_len=64)
+    slots, po, pl = L.paged_attn_workspace(a)
+    assert slots == 1 and po == 0 and pl == 0
+    a = _good_args(L, num_splits=0, max_context_len=64, block_table_stride=1000)
+    a.max_context_len = 5000   # > 2048 tokens per matrix-core partition
+    slots, po, pl = L.paged_attn_workspace(a)
+    assert slots == 3 and po == 3 * 10 * 16 * 128 and pl == 3 * 10 * 16
+    a = _good_args(L, num_splits=64, block_table_stride=1000, max_context_len=16000)
+    assert L.paged_attn_workspace(a)[0] == 64
+    # decode rows (g * q_len < 16) use the vector kernel's 1024-token partitions
+    a = _good_args(L, num_splits=0, max_q_len=1, min_q_len=1, block_table_stride=1000, max_context_len=5000)
+    assert L.paged_attn_workspace(a)[0] == 5
+
+
+def test_empty_batch_is_ok_without_pointers():
+    L = _lib()
+    lib = L.load_library()
+    a = _good_args(L, batch=0, total_q=0, q=0, k_cache=0)
+    assert lib.ra_paged_attn(ctypes.byref(a), None) == 0
+
+
+def _store(lib, **kw):
+    args = dict(k=FAKE, v=FAKE, src=1, ks=256, vs=256, slots=FAKE, n=4, kc=FAKE, vc=FAKE, kv=2, pages=10,
+                hkv=2, d=128, page=16, ksc=0.1, vsc=0.1)
+    args.update(kw)
+    return lib.ra_kv_store(args["k"], args["v"], args["src"], args["ks"], args["vs"], args["slots"], args["n"],
+                           args["kc"], args["vc"], args["kv"], args["pages"], args["hkv"], args["d"], args["page"],
+                           args["ksc"], args["vsc"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(n=-1), 1, "num_tokens"),
+    (dict(src=3), 2, "src_dtype"),
+    (dict(kv=0), 2, "kv_dtype"),
+    (dict(d=32), 2, "head_dim"),
+    (dict(page=8), 2, "page_size"),
+    (dict(hkv=0), 1, "num_kv_heads"),
+    (dict(pages=0), 1, "num_pages"),
+    (dict(ksc=0.0), 1, "no fallback"),
+    (dict(vsc=float("nan")), 1, "no fallback"),
+    (dict(ks=100), 1, "strides"),
+    (dict(k=0), 1, "non-NULL"),
+    (dict(kc=FAKE + 1), 3, "aligned"),
+    (dict(ks=260), 3, "multiples of 8"),
+])
+def test_store_validation(kw, status, msg):
+    L = _lib()
+    lib = L.load_library()
+    st = _store(lib, **kw)
+    assert st == status, (st, lib.ra_last_error())
+    assert msg in lib.ra_last_error().decode()
+
+
+def test_store_zero_tokens_ok_and_fp16_ignores_scale():
+    L = _lib()
+    lib = L.load_library()
+    assert _store(lib, n=0, k=0) == 0
+    assert _store(lib, n=0, kv=1, ksc=0.0) == 0
+
+
+@pytest.mark.parametrize("args,status,msg", [
+    ((FAKE, FAKE, 0, 10, 128, FAKE, 1, FAKE), 1, "num_partitions"),
+    ((FAKE, FAKE, 5000, 10, 128, FAKE, 1, FAKE), 1, "num_partitions"),
+    ((FAKE, FAKE, 2, -1, 128, FAKE, 1, FAKE), 1, "rows"),
+    ((FAKE, FAKE, 2, 10, 80, FAKE, 1, FAKE), 2, "head_dim"),
+    ((FAKE, FAKE, 2, 10, 128, FAKE, 7, FAKE), 2, "out_dtype"),
+    ((0, FAKE, 2, 10, 128, FAKE, 1, FAKE), 1, "non-NULL"),
+    ((FAKE + 4, FAKE, 2, 10, 128, FAKE, 1, FAKE), 3, "aligned"),
+])
+def test_merge_validation(args, status, msg):
+    L = _lib()
+    lib = L.load_library()
+    st = lib.ra_lse_merge(*args, None)
+    assert st == status and msg in lib.ra_last_error().decode()
+    assert lib.ra_lse_merge(FAKE, FAKE, 2, 0, 128, FAKE, 1, None, None) == 0
+
+
+@pytest.mark.parametrize("args,status,msg", [
+    ((FAKE, 2, 2, 0.1, FAKE, 16, 4, 1, 128, FAKE), 1, "which"),
+    ((FAKE, 0, 5, 0.1, FAKE, 16, 4, 1, 128, FAKE), 2, "kv_dtype"),
+    ((FAKE, 0, 2, 0.1, FAKE, 16, 4, 1, 48, FAKE), 2, "head_dim"),
+    ((FAKE, 0, 2, 0.0, FAKE, 16, 4, 1, 128, FAKE), 1, "scale"),
+    ((FAKE, 0, 2, 0.1, FAKE, -1, 4, 1, 128, FAKE), 1, "ctx"),
+    ((0, 0, 2, 0.1, FAKE, 16, 4, 1, 128, FAKE), 1, "non-NULL"),
+    ((FAKE + 2, 0, 2, 0.1, FAKE, 16, 4, 1, 128, FAKE), 3, "aligned"),
+])
+def test_gather_validation(args, status, msg):
+    L = _lib()
+    lib = L.load_library()
+    st = lib.ra_kv_gather_dequant(*args, None)
+    assert st == status and msg in lib.ra_last_error().decode()

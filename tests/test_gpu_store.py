@@ -1,0 +1,164 @@
+"""GPU parity of ra_kv_store and ra_kv_gather_dequant against the oracle.
+
+Bit-exact: cache bytes after the store equal the oracle's scatter of its
+quantised codes into the same sentinel-filled cache; the gather returns the
+oracle's fp32 dequantised values bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import paged_quantized_kv_ra_amd as P
+from oracle import codecs as OC
+from oracle import layout as OL
+from paged_quantized_kv_ra_amd import workloads as W
+from tests.gpu_util import DeviceWorkload, log
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_cache(w, which):
+    e = 2 if w.kv_dtype == "f16" else 1
+    nbytes = w.num_pages * w.num_kv_heads * 16 * w.head_dim * e
+    if w.kv_dtype == "f16":
+        cache = np.frombuffer(np.full(nbytes // 2, w.cache_sentinel, np.uint16).tobytes(), np.uint8).copy()
+    else:
+        cache = np.full(nbytes, w.cache_sentinel, np.uint8)
+    src = w.tokens_k if which == "k" else w.tokens_v
+    scale = w.k_scale if which == "k" else w.v_scale
+    codes = OC.quantize(OC.source_to_f32(src, w.src_dtype), w.kv_dtype, scale)
+    return OL.scatter(cache, codes, w.token_slots, which, w.num_kv_heads, w.head_dim, w.kv_dtype)
+
+
+def _gpu_bytes(t):
+    return t.contiguous().view(torch.uint8).cpu().numpy().reshape(-1)
+
+
+@pytest.mark.parametrize("kv", ["f16", "e4m3", "int8"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("src", ["f16", "bf16"])
+def test_store_bit_exact_small(kv, D, src):
+    w = W.build(f"store_{kv}_{D}_{src}", 11, ctx=[50, 33, 70, 16, 1], q_len=1, num_q_heads=4, num_kv_heads=2,
+                head_dim=D, kv_dtype=kv, src_dtype=src, q_dtype="f16", pool_pages=24)
+    dw = DeviceWorkload(w)
+    torch.cuda.synchronize()
+    for which, cache in (("k", dw.k_cache), ("v", dw.v_cache)):
+        got = _gpu_bytes(cache)
+        want = _oracle_cache(w, which)
+        assert got.shape == want.shape
+        diff = np.nonzero(got != want)[0]
+        assert diff.size == 0, f"{which}: {diff.size} bytes differ, first at {diff[:8]}"
+
+
+def _all_16bit_tokens(src, D):
+    """Every 16-bit pattern of the source dtype, as [65536 / D][1][D]."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    if src == "f16":
+        return bits.view(np.float16).reshape(-1, 1, D)
+    return bits.reshape(-1, 1, D)
+
+
+@pytest.mark.parametrize("kv", ["e4m3", "int8", "f16"])
+@pytest.mark.parametrize("src", ["f16", "bf16"])
+@pytest.mark.parametrize("scale", [1.0, 0.0130004883, 2.0 ** -7, 3.7e-3, 1000.0])
+def test_store_every_16bit_input(kv, src, scale):
+    """Exhaustive over the store's reachable inputs for a given scale: every
+    fp16 / bf16 bit pattern (NaN, inf, subnormals, ties) through the fp32
+    divide and the encoder."""
+    D = 128
+    x = _all_16bit_tokens(src, D)
+    T = x.shape[0]
+    pages = T // 16
+    slots = np.random.default_rng(1).permutation(T).astype(np.int64)
+    kc = P.new_cache(pages, 1, D, kv, fill=0)
+    vc = P.new_cache(pages, 1, D, kv, fill=0)
+    xt = torch.from_numpy(x.view(np.int16)).cuda()
+    xt = xt.view(torch.float16) if src == "f16" else xt.view(torch.bfloat16)
+    P.kv_store(xt, xt, torch.from_numpy(slots).cuda(), kc, vc, kv, scale, scale)
+    torch.cuda.synchronize()
+    codes = OC.quantize(OC.source_to_f32(x, src), kv, scale)
+    e = 2 if kv == "f16" else 1
+    zero = np.zeros(pages * 16 * D * e, np.uint8)
+    for which, cache in (("k", kc), ("v", vc)):
+        want = OL.scatter(zero, codes, slots, which, 1, D, kv)
+        got = _gpu_bytes(cache)
+        if kv == "f16":   # NaN payloads may differ only in quiet bits; compare values
+            g16, w16 = got.view(np.float16), want.view(np.float16)
+            same = (g16.view(np.uint16) == w16.view(np.uint16)) | (np.isnan(g16) & np.isnan(w16))
+            assert same.all(), f"{which}: {(~same).sum()} differ"
+        else:
+            diff = np.nonzero(got != want)[0]
+            assert diff.size == 0, f"{which}: {diff.size} bytes differ"
+
+
+def test_store_skips_negative_and_out_of_range_slots():
+    D, hkv, pages = 64, 2, 4
+    kc = P.new_cache(pages, hkv, D, "e4m3", fill=0x5A)
+    vc = P.new_cache(pages, hkv, D, "e4m3", fill=0x5A)
+    rng = np.random.default_rng(2)
+    x = torch.from_numpy(rng.standard_normal((4, hkv, D)).astype(np.float16)).cuda()
+    slots = torch.tensor([-1, 5, pages * 16, -100], dtype=torch.int64).cuda()
+    P.kv_store(x, x, slots, kc, vc, "e4m3", 0.01, 0.01)
+    torch.cuda.synchronize()
+    got = _gpu_bytes(kc)
+    cache0 = np.full(got.size, 0x5A, np.uint8)
+    codes = OC.quantize(x.cpu().numpy().astype(np.float32), "e4m3", 0.01)
+    want = OL.scatter(cache0, codes, np.array([-1, 5, -1, -1]), "k", hkv, D, "e4m3")
+    assert np.array_equal(got, want)
+
+
+def test_store_strided_source_view():
+    """K and V may be views into a fused [T][3][Hkv][D] QKV buffer."""
+    D, hkv, T = 128, 2, 40
+    rng = np.random.default_rng(3)
+    qkv = torch.from_numpy(rng.standard_normal((T, 3, hkv, D)).astype(np.float16)).cuda()
+    k, v = qkv[:, 1], qkv[:, 2]
+    assert k.stride(0) == 3 * hkv * D
+    slots = torch.from_numpy(rng.permutation(64)[:T].astype(np.int64)).cuda()
+    kc = P.new_cache(4, hkv, D, "int8", fill=0)
+    vc = P.new_cache(4, hkv, D, "int8", fill=0)
+    P.kv_store(k, v, slots, kc, vc, "int8", 0.02, 0.03)
+    torch.cuda.synchronize()
+    for which, src, sc, cache in (("k", k, 0.02, kc), ("v", v, 0.03, vc)):
+        codes = OC.quantize(src.cpu().numpy().astype(np.float32), "int8", sc)
+        want = OL.scatter(np.zeros(4 * hkv * 16 * D, np.uint8), codes, slots.cpu().numpy(), which, hkv, D, "int8")
+        assert np.array_equal(_gpu_bytes(cache), want)
+
+
+@pytest.mark.parametrize("kv", ["e4m3", "int8"])
+@pytest.mark.parametrize("which", [0, 1])
+@pytest.mark.parametrize("D", [64, 128])
+def test_gather_dequant_every_code(kv, which, D):
+    """Every byte value decodes exactly: fp32(decode(code)) * scale."""
+    hkv, pages = 2, 8
+    n = pages * hkv * 16 * D
+    raw = np.arange(n, dtype=np.int64) % 256
+    raw = np.random.default_rng(D + which).permutation(raw).astype(np.uint8)
+    cache = torch.from_numpy(raw.reshape(pages, hkv, 16 * D)).cuda()
+    bt = torch.from_numpy(np.random.default_rng(4).permutation(pages).astype(np.int32)).cuda()
+    ctx = pages * 16
+    scale = 0.0130004883
+    got = P.kv_gather_dequant(cache, which, kv, scale, bt, ctx, D).cpu().numpy()
+    slots = OL.slots_for_sequence(bt.cpu().numpy(), ctx)
+    codes = OL.gather(raw, slots, "k" if which == 0 else "v", hkv, D, kv)
+    want = OC.dequantize(codes, kv, scale)
+    both_nan = np.isnan(got) & np.isnan(want)
+    same = (got.view(np.uint32) == want.view(np.uint32)) | both_nan
+    assert same.all(), f"{(~same).sum()} values differ"
+    if kv == "e4m3":
+        assert both_nan.sum() == 2 * (n // 256)      # codes 0x7F and 0xFF
+
+
+def test_gather_dequant_f16_and_bad_page():
+    D, hkv, pages = 64, 1, 3
+    rng = np.random.default_rng(5)
+    vals = rng.standard_normal(pages * hkv * 16 * D).astype(np.float16)
+    cache = torch.from_numpy(vals.reshape(pages, hkv, 16 * D)).cuda()
+    bt = torch.tensor([2, 99, 0], dtype=torch.int32).cuda()     # 99 is not a page
+    got = P.kv_gather_dequant(cache, 0, "f16", 1.0, bt, 40, D).cpu().numpy()
+    codes = OL.gather(vals.view(np.uint8), OL.slots_for_sequence([2, 0, 0], 40), "k", hkv, D, "f16")
+    want = codes.astype(np.float32)
+    assert np.array_equal(got[:16], want[:16])
+    assert np.isnan(got[16:32]).all()
+    assert np.array_equal(got[32:], want[32:])
+    log("gather ok")
