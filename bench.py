@@ -1,0 +1,297 @@
+#!/usr/bin/env python3
+"""Benchmark of one decode/verify step of paged, quantized-KV attention on one MI355X.
+
+A step is the whole hot path over one batch: ra_kv_store of the step's new
+K/V rows (the 1 + 4 verify tokens of every sequence), ra_paged_attn over the
+paged cache (partials per KV partition) and ra_lse_merge.  Inputs are seeded
+synthetic data already resident in HBM.  Each step uses the next of L
+identical copies of the KV pool (at least 1 GiB in total), the way successive
+layers of a model read distinct caches, so the 256 MB Infinity Cache cannot
+serve repeated reads.
+
+Output: one JSON line.  `value` is KV tokens attended per second over the
+timed steps; `roofline` is the attention kernel's algorithmic HBM bytes per
+launch over its average duration (HIP events on the launch stream);
+`cpu_baseline` is the CPU oracle timed on a bounded sample of the same step.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PEAK_HBM_GBS = 8000.0
+POOL_ROTATION_BYTES = 1 << 30
+KERNEL_SOURCES = ["paged_quantized_kv_ra_amd/csrc/attn_mfma.hip", "paged_quantized_kv_ra_amd/csrc/attn_vec.hip",
+                  "paged_quantized_kv_ra_amd/csrc/attn_common.h", "paged_quantized_kv_ra_amd/csrc/ra_device.h",
+                  "paged_quantized_kv_ra_amd/csrc/ra_internal.h"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--workload", default="verify_fp8_32k")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain device copy of known size (for counter scaling)")
+    return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain 1 GiB device-to-device copy, for scaling HBM byte counters."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copied {n} bytes x3")
+
+
+class Step:
+    """Device state and prebuilt C-ABI argument blocks for one workload."""
+
+    def __init__(self, w):
+        import torch
+        import paged_quantized_kv_ra_amd as P
+        from paged_quantized_kv_ra_amd import _lib as L
+        self.w, self.L, self.P = w, L, P
+        self.lib = L.load_library()
+        dev = "cuda"
+        D, hkv = w.head_dim, w.num_kv_heads
+        # one pool filled through the store, then cloned
+        k0 = P.new_cache(w.num_pages, hkv, D, w.kv_dtype, dev, fill=w.cache_sentinel)
+        v0 = P.new_cache(w.num_pages, hkv, D, w.kv_dtype, dev, fill=w.cache_sentinel)
+        U = w.tokens_k.shape[0]
+        chunk = 1 << 18
+        for lo in range(0, U, chunk):
+            hi = min(U, lo + chunk)
+            P.kv_store(self._src(w.tokens_k[lo:hi]), self._src(w.tokens_v[lo:hi]),
+                       torch.from_numpy(w.token_slots[lo:hi]).to(dev), k0, v0, w.kv_dtype, w.k_scale, w.v_scale)
+        pool_bytes = 2 * k0.numel() * k0.element_size()
+        self.copies = max(1, -(-POOL_ROTATION_BYTES // pool_bytes))
+        self.pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(self.copies - 1)]
+        torch.cuda.synchronize()
+        # this step's new tokens: the last q_len positions of every sequence
+        rows = w.new_token_rows()
+        self.k_new = self._src(w.tokens_k[rows])
+        self.v_new = self._src(w.tokens_v[rows])
+        self.slots_new = torch.from_numpy(w.token_slots[rows]).to(dev)
+        self.q = self._src(w.q) if w.q_dtype == "f16" else self._src_bf16(w.q)
+        self.bt = torch.from_numpy(w.block_tables).to(dev)
+        self.ctx = torch.from_numpy(w.ctx).to(dev)
+        self.qsl = torch.from_numpy(w.query_start_loc).to(dev)
+        T, hq = self.q.shape[0], self.q.shape[1]
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty((T, hq), dtype=torch.float32, device=dev)
+        self.args = []
+        for k, v in self.pools:
+            a = L._attn_args(self.q, k, v, self.bt, self.ctx, self.qsl, w.kv_dtype, w.k_scale, w.v_scale,
+                             w.softmax_scale, w.max_q_len, int(w.q_len.min()), w.max_context_len,
+                             w.window_left, w.num_sinks, w.num_splits, hkv)
+            self.args.append(a)
+        self.slots, po_n, _ = L.paged_attn_workspace(self.args[0])
+        self.po = torch.empty((self.slots, T, hq, D), dtype=torch.float32, device=dev)
+        self.pl = torch.empty((self.slots, T, hq), dtype=torch.float32, device=dev)
+        for a in self.args:          # partials only: the merge is launched separately
+            a.partial_out = self.po.data_ptr()
+            a.partial_lse = self.pl.data_ptr()
+            a.partial_slots = self.slots
+        self.rows = T * hq
+        self.q_code = L.RA_F16 if w.q_dtype == "f16" else L.RA_BF16
+        self.kv_code = L.KV_CODES[w.kv_dtype]
+
+    @staticmethod
+    def _src(x):
+        import numpy as np
+        import torch
+        return torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
+
+    @staticmethod
+    def _src_bf16(x):
+        import numpy as np
+        import torch
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to("cuda").view(torch.bfloat16)
+
+    def run(self, i, stream, ev=None):
+        """Enqueue step i: store, attention (between the two events), merge."""
+        w, lib, L = self.w, self.lib, self.L
+        k, v = self.pools[i % self.copies]
+        s = ctypes.c_void_p(stream)
+        st = lib.ra_kv_store(self.k_new.data_ptr(), self.v_new.data_ptr(), L.RA_F16, self.k_new.stride(0),
+                             self.v_new.stride(0), self.slots_new.data_ptr(), self.k_new.shape[0], k.data_ptr(),
+                             v.data_ptr(), self.kv_code, w.num_pages, w.num_kv_heads, w.head_dim, 16,
+                             w.k_scale, w.v_scale, s)
+        if ev is not None:
+            ev[0].record()
+        st |= lib.ra_paged_attn(ctypes.byref(self.args[i % self.copies]), s)
+        if ev is not None:
+            ev[1].record()
+        st |= lib.ra_lse_merge(self.po.data_ptr(), self.pl.data_ptr(), self.slots, self.rows, w.head_dim,
+                               self.out.data_ptr(), self.q_code, self.lse.data_ptr(), s)
+        if st != 0:
+            raise RuntimeError(lib.ra_last_error().decode())
+
+
+def algorithmic_bytes(w):
+    """HBM bytes one attention launch must move: the visible KV tokens' codes
+    (2 * Hkv * D * e per token), the block-table entries of the visited pages
+    (4 B per 16 tokens per sequence) and the queries."""
+    kv = w.kv_bytes_attended()
+    bt = 4 * sum(-(-int(c) // 16) for c in w.ctx)
+    q = w.q.nbytes
+    return kv + bt + q
+
+
+def cpu_baseline(w, seconds):
+    """The oracle (numpy, fp64) on whole sequences of the same step, until
+    about `seconds` of CPU time: dequantise the cached codes, then attend."""
+    sys.path.insert(0, ROOT)
+    from oracle import attention as OA
+    from oracle import codecs as OC
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    g = w.num_q_heads // w.num_kv_heads
+    done_tokens, elapsed, seqs = 0, 0.0, 0
+    b = 0
+    codes = {}
+    while elapsed < seconds and seqs < 64 * w.batch:
+        if b % w.batch not in codes:       # the cache contents: made once, not timed
+            rows = w.seq_rows[b % w.batch]
+            codes[b % w.batch] = (
+                OC.quantize(OC.source_to_f32(w.tokens_k[rows], w.src_dtype), w.kv_dtype, w.k_scale),
+                OC.quantize(OC.source_to_f32(w.tokens_v[rows], w.src_dtype), w.kv_dtype, w.v_scale))
+        kc, vc = codes[b % w.batch]
+        q0, q1 = int(w.query_start_loc[b % w.batch]), int(w.query_start_loc[b % w.batch + 1])
+        q = OC.source_to_f32(w.q[q0:q1], w.q_dtype).astype("float64")
+        t = time.perf_counter()
+        k = OC.dequantize(kc, w.kv_dtype, w.k_scale)
+        v = OC.dequantize(vc, w.kv_dtype, w.v_scale)
+        OA.attention(q, k, v, w.softmax_scale, w.window_left, w.num_sinks)
+        elapsed += time.perf_counter() - t
+        done_tokens += OA.attended_keys(int(w.ctx[b % w.batch]), q1 - q0, w.window_left, w.num_sinks)
+        seqs += 1
+        b += 1
+    return {"value": done_tokens / elapsed, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{seqs} whole sequences (all {w.num_kv_heads} KV heads x {g} query heads) of "
+                      f"{w.name}: dequantise + fp64 attention, {elapsed:.1f} s"}
+
+
+def traffic_from_profile(wname, src_hash):
+    """HBM bytes per attention launch from committed rocprofv3 counters, if
+    they were taken on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", f"attn_traffic_{wname}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("kernel_source_hash") != src_hash:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this path is single-GPU "
+              "by design and has no multi-GPU mode.", file=sys.stderr)
+        sys.exit(2)
+    sys.path.insert(0, ROOT)
+    import torch
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    from paged_quantized_kv_ra_amd import workloads as W
+    make = W.BENCH_WORKLOADS[args.workload]
+    t0 = time.time()
+    w = make()
+    log(f"built {w.name} in {time.time() - t0:.1f}s")
+    step = Step(w)
+    log(f"pool copies: {step.copies}, partition slots: {step.slots}")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    for i in range(args.warmup):
+        step.run(i, sp)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step.run(args.warmup + i, sp, evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(stop)
+    attn_ms = [a.elapsed_time(b) for a, b in evs]
+    attn_avg_ms = sum(attn_ms) / len(attn_ms)
+    ms_per_step = total_ms / args.steps
+    tokens = w.attended_keys()
+    value = tokens / (ms_per_step / 1e3)
+    alg = algorithmic_bytes(w)
+    achieved = alg / (attn_avg_ms / 1e3) / 1e9
+    src_hash = kernel_source_hash()
+    traffic = traffic_from_profile(w.name, src_hash)
+    log(f"{args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us/step), "
+        f"attention {attn_avg_ms * 1e3:.1f} us avg, {achieved:.0f} GB/s algorithmic")
+    line = {
+        "metric": "KV tokens attended/sec and achieved HBM GB/s (% of MI355X peak), FP8 KV @32K",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "context": int(w.ctx.max()), "q_len": w.max_q_len,
+                   "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "kv_dtype": w.kv_dtype, "page_size": 16, "partition_slots": step.slots,
+                   "kv_pool_copies": step.copies, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic, "kernel": "attn_mfma_kernel" if w.num_q_heads // w.num_kv_heads
+                     * w.max_q_len >= 16 else "attn_vec_kernel",
+                     "algorithmic_bytes_per_launch": alg, "attn_us": round(attn_avg_ms * 1e3, 2),
+                     "kernel_source_hash": src_hash},
+        "attended_tokens_per_step": tokens,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle sample ...")
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

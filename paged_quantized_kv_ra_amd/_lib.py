@@ -15,7 +15,8 @@ import os
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libra_kv.so")
+# RA_KV_LIB selects another build of the library (same ABI); default: the in-tree one
+LIB_PATH = os.environ.get("RA_KV_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libra_kv.so")
 
 RA_OK, RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED, RA_ERR_MISALIGNED, RA_ERR_WORKSPACE, RA_ERR_HIP = range(6)
 RA_F16, RA_BF16, RA_F32 = 1, 2, 3

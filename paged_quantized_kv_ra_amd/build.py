@@ -51,27 +51,39 @@ def torch_lib_dir():
     return d
 
 
-def _compile(src, extra):
-    obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + HIP_FLAGS + extra + ["-c", src, "-o", obj]
+# Per-file code-generation options.  The matrix-core attention keeps its MFMA
+# accumulators in architectural VGPRs: with everything in VGPRs it fits two
+# waves per SIMD and avoids AGPR <-> VGPR copies around the softmax.
+FILE_FLAGS = {
+    "attn_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
+def _compile(src, extra, objdir=OBJDIR):
+    obj = os.path.join(objdir, os.path.basename(src) + ".o")
+    cmd = [HIPCC] + HIP_FLAGS + FILE_FLAGS.get(os.path.basename(src), []) + extra + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj, r.stderr
 
 
-def build(jobs=None, verbose=False, extra=None):
-    """Compile every csrc/*.hip for gfx950 and link libra_kv.so.  Always rebuilds."""
+def build(jobs=None, verbose=False, extra=None, out=LIB, objdir=OBJDIR):
+    """Compile every csrc/*.hip for gfx950 and link libra_kv.so.  Always rebuilds.
+
+    ``extra``: additional hipcc flags; ``out`` / ``objdir``: where the library
+    and the objects go (the in-tree paths by default).
+    """
     if not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
-    os.makedirs(OBJDIR, exist_ok=True)
+    os.makedirs(objdir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     if not srcs:
         raise RuntimeError("no HIP sources")
     extra = list(extra or [])
     jobs = jobs or min(8, os.cpu_count() or 4)
     with cf.ThreadPoolExecutor(jobs) as ex:
-        results = list(ex.map(lambda s: _compile(s, extra), srcs))
+        results = list(ex.map(lambda s: _compile(s, extra, objdir), srcs))
     objs = [o for o, _ in results]
     if verbose:
         for (o, err), s in zip(results, srcs):
@@ -80,15 +92,15 @@ def build(jobs=None, verbose=False, extra=None):
             if warn:
                 print(f"[{os.path.basename(s)}]\n{warn}", file=sys.stderr)
     tl = torch_lib_dir()
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [CLANGXX, "-shared", "-fPIC", "-o", tmp] + objs + [
         f"-L{tl}", "-l:libamdhip64.so", f"-Wl,-rpath,{tl}", "-Wl,--no-undefined",
         "-Wl,-z,defs"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    shutil.move(tmp, LIB)
-    return LIB
+    shutil.move(tmp, out)
+    return out
 
 
 def main():

@@ -7,78 +7,80 @@
 // pages' V100 converts stored KV to FP16 for the arithmetic: ReVolta README,
 // "Weight and KV formats").
 //
-// Per wavefront and pair of 16-token pages:
-//   S^T[32 keys][16 rows]  = K[32][D] . Q^T[D][16]     v_mfma_f32_16x16x32_f16, per 16-row tile
-//   P^T = exp2(c * S^T - c * m)   (online softmax, fp32, rescaled lazily)
-//   O^T[D][16 rows]       += V^T[D][32] . P^T[32][16]
+// Per wavefront and 16-token page, for each 16-row tile of query rows:
+//   S^T[16 keys][16 rows] = K[16][D] . Q^T[D][16]      v_mfma_f32_16x16x32_f16 (D/32 steps)
+//   P^T = exp2(c * S^T - c * m)                       online softmax, fp32, rescaled lazily
+//   O^T[D][16 rows]      += V^T[D][16] . P^T[16][16]   v_mfma_f32_16x16x16_f16 (D/16 tiles)
 // The cache layout puts every lane's 16-byte loads directly in the operand
 // order of both products: a K lane holds one token's contiguous D/4 dims, a V
 // lane holds four consecutive tokens of D/16 dims, and the S^T accumulator
 // layout (lane = row + 16 * token-quad) is exactly the P^T operand layout, so
-// no data moves between lanes or through LDS in the hot loop.
+// no data moves between lanes or through LDS in the hot loop.  Pages stream
+// through a ring of NBUF register buffers, NBUF - 1 pages in flight per wave.
 //
-// A workgroup has 4 waves that take page pairs round-robin; their partial
+// A workgroup has 8 waves (two per SIMD) that take pages round-robin; their partial
 // (m, l, O) are combined through LDS in a fixed order at the end.
 #include "attn_common.h"
 
 namespace ra {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;   // waves per workgroup (two per SIMD)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;   // log2 headroom before the running max is refreshed
 
+// depth of the per-wave page ring (tuning constants)
+#ifndef RA_MFMA_RING_8BIT
+#define RA_MFMA_RING_8BIT 2
+#endif
+#ifndef RA_MFMA_RING_16BIT
+#define RA_MFMA_RING_16BIT 2
+#endif
+
 template <int KV, int D>
 struct Geo {
   static constexpr int E = KV == KV_F16 ? 2 : 1;
-  static constexpr int SLABS = D * E / 64;       // 16-byte loads per lane per page
+  static constexpr int SLABS = D * E / 64;       // 16-byte loads per lane per page (K, and again V)
   static constexpr int KS = D / 32;              // k-steps of the QK product
   static constexpr int MT = D / 16;              // 16-dim tiles of the PV product
   static constexpr int BLK = kPage * D * E;      // bytes per (page, head) block
+  // register buffers of the page ring: one page (K and V) is 8 * SLABS VGPRs
+  static constexpr int NBUF = E == 1 ? RA_MFMA_RING_8BIT : RA_MFMA_RING_16BIT;
 };
 
 template <int KV, int D>
-struct PairRegs {
-  u32x4 k[2][Geo<KV, D>::SLABS];
-  u32x4 v[2][Geo<KV, D>::SLABS];
+struct PageRegs {
+  u32x4 k[Geo<KV, D>::SLABS];
+  u32x4 v[Geo<KV, D>::SLABS];
 };
 
-// Issue the loads of page pair `p` (logical pages 2p, 2p+1 of the unit).
+// Issue the loads of the wave's i-th page (logical page wave + 4 i of the
+// unit).  Branch-free: a page past the unit's end loads page 0 and is never
+// computed, so the compiler can keep the next pages' loads in flight.
 template <int KV, int D>
-__device__ __forceinline__ void load_pair(PairRegs<KV, D>& r, const AttnLaunch& a, const UnitPages& pg,
-                                          int32_t npages, int32_t p, const int32_t* bt_row, int h,
-                                          uint32_t lane_off, bool& bad) {
+__device__ __forceinline__ void load_page(PageRegs<KV, D>& r, PageIdChunks& ids, const AttnLaunch& a,
+                                          const UnitPages& pg, int32_t npages, int32_t wave, int32_t i,
+                                          const int32_t* bt_row, int h, uint32_t lane_off, int lane, bool& bad) {
   using G = Geo<KV, D>;
+  const bool live = wave_page<1, kWaves>(wave, i) < npages;
+  const int32_t pid = page_id<1, kWaves>(ids, a, pg, npages, bt_row, wave, i, lane, live, bad);
+  const int64_t blk = ((int64_t)pid * a.hkv + h) * G::BLK;
+  const uint8_t* kp = a.k_cache + blk + lane_off;
+  const uint8_t* vp = a.v_cache + blk + lane_off;
 #pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int32_t n = 2 * p + x;
-    int32_t pid = -1;
-    if (n < npages) {
-      pid = bt_row[pg.page(n)];
-      if (pid < 0 || pid >= a.num_pages) { bad = true; pid = -1; }
-    }
-    if (pid >= 0) {
-      const int64_t blk = ((int64_t)pid * a.hkv + h) * G::BLK;
-      const uint8_t* kp = a.k_cache + blk + lane_off;
-      const uint8_t* vp = a.v_cache + blk + lane_off;
+  for (int j = 0; j < G::SLABS; ++j) r.k[j] = load16(kp + j * 1024);
 #pragma unroll
-      for (int j = 0; j < G::SLABS; ++j) r.k[x][j] = load16(kp + j * 1024);
-#pragma unroll
-      for (int j = 0; j < G::SLABS; ++j) r.v[x][j] = load16(vp + j * 1024);
-    } else {
-#pragma unroll
-      for (int j = 0; j < G::SLABS; ++j) { r.k[x][j] = u32x4{0, 0, 0, 0}; r.v[x][j] = u32x4{0, 0, 0, 0}; }
-    }
-  }
+  for (int j = 0; j < G::SLABS; ++j) r.v[j] = load16(vp + j * 1024);
 }
 
+// K operand of k-step ks: the lane's token, dims kgrp * D/4 + 8 ks .. + 8.
 template <int KV, int D>
-__device__ __forceinline__ f16x8 k_operand(const PairRegs<KV, D>& r, int x, int ks) {
+__device__ __forceinline__ f16x8 k_operand(const PageRegs<KV, D>& r, int ks) {
   if constexpr (KV == KV_F16) {
-    return as<f16x8>(r.k[x][ks]);
+    return as<f16x8>(r.k[ks]);
   } else {
-    const u32x4 w = r.k[x][ks >> 1];
+    const u32x4 w = r.k[ks >> 1];
     const uint32_t d0 = (ks & 1) ? w[2] : w[0];
     const uint32_t d1 = (ks & 1) ? w[3] : w[1];
     const f16x4 lo = codes4_to_f16x4<KV>(d0);
@@ -87,18 +89,18 @@ __device__ __forceinline__ f16x8 k_operand(const PairRegs<KV, D>& r, int x, int 
   }
 }
 
-// Four consecutive tokens (of page x) of dim tile mt, as fp16.
+// V operand of dim tile mt: tokens 4 kgrp .. 4 kgrp + 3 of the lane's dim.
 template <int KV, int D>
-__device__ __forceinline__ f16x4 v_quad(const PairRegs<KV, D>& r, int x, int mt) {
+__device__ __forceinline__ f16x4 v_operand(const PageRegs<KV, D>& r, int mt) {
   if constexpr (KV == KV_F16) {
-    const u32x4 w = r.v[x][mt >> 1];
+    const u32x4 w = r.v[mt >> 1];
     const uint32_t a = (mt & 1) ? w[2] : w[0];
     const uint32_t b = (mt & 1) ? w[3] : w[1];
     const f16x2 lo = as<f16x2>(a);
     const f16x2 hi = as<f16x2>(b);
     return f16x4{lo[0], lo[1], hi[0], hi[1]};
   } else {
-    const u32x4 w = r.v[x][mt >> 2];
+    const u32x4 w = r.v[mt >> 2];
     return codes4_to_f16x4<KV>(w[mt & 3]);
   }
 }
@@ -111,62 +113,57 @@ struct Acc {
 };
 
 template <int KV, int D, int NT>
-__device__ __forceinline__ void compute_pair(Acc<KV, D, NT>& acc, const PairRegs<KV, D>& r,
-                                             const f16x8 (&qf)[NT][Geo<KV, D>::KS],
-                                             const AttnLaunch& a, const UnitPages& pg, int32_t npages,
-                                             int32_t p, int32_t ctx, int32_t q_len,
-                                             const int32_t (&pos)[NT], int kgrp, float c, float thr) {
+__device__ __forceinline__ void compute_page(Acc<KV, D, NT>& acc, PageRegs<KV, D>& r,
+                                             const f16x8 (*sm_q)[Geo<KV, D>::KS][kWave], int lane,
+                                             const AttnLaunch& a, const UnitPages& pg, int32_t n, int32_t ctx,
+                                             int32_t q_len, const int32_t (&pos)[NT], int kgrp, float c,
+                                             float thr) {
   using G = Geo<KV, D>;
-  // ---- scores: S^T tiles for both pages
-  f32x4 s[2][NT];
+  // ---- scores S^T for the page's 16 keys
+  f32x4 s[NT];
 #pragma unroll
-  for (int x = 0; x < 2; ++x) {
+  for (int nt = 0; nt < NT; ++nt) s[nt] = f32x4{0, 0, 0, 0};
+  // the query fragments are re-read from LDS for every page (an opaque index
+  // keeps the compiler from hoisting them into registers for the whole loop)
+  int li = lane;
+  asm volatile("" : "+v"(li));
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) s[x][nt] = f32x4{0, 0, 0, 0};
+  for (int ks = 0; ks < G::KS; ++ks) {
+    const f16x8 kop = k_operand<KV, D>(r, ks);
 #pragma unroll
-    for (int ks = 0; ks < G::KS; ++ks) {
-      const f16x8 kop = k_operand<KV, D>(r, x, ks);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        s[x][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qf[nt][ks], s[x][nt], 0, 0, 0);
-    }
+    for (int nt = 0; nt < NT; ++nt)
+      s[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, sm_q[nt][ks][li], s[nt], 0, 0, 0);
   }
-  // ---- masks (only for pairs that can hold an invisible key)
-  const int32_t n0 = 2 * p;
-  const bool has_b = n0 + 1 < npages;
-  const int32_t tok0 = pg.page(n0) * kPage;
-  const int32_t tok1 = has_b ? pg.page(n0 + 1) * kPage : tok0;
-  const bool need_mask = !has_b || (tok1 + kPage - 1 > ctx - q_len) ||
-                         (a.window >= 0 && tok0 <= ctx - q_len - a.window);
-  uint32_t vlive[2] = {0xFu, 0xFu};   // per page: bit i set where token 4*kgrp+i holds data
-  bool sanitize = false;
+  // ---- masks (only on pages that can hold an invisible key).  Keys past ctx
+  // (stale bytes of the last page) also get their V codes zeroed so that
+  // 0 * garbage cannot produce NaN.
+  const int32_t tok0 = pg.page(n) * kPage;
+  const bool need_mask = (tok0 + kPage - 1 > ctx - q_len) || (a.window >= 0 && tok0 <= ctx - 1 - a.window);
   if (need_mask) {
+    const int32_t tb = tok0 + 4 * kgrp;
+    uint32_t keep8 = 0, keep_lo = 0, keep_hi = 0;   // byte / half masks of the lane's 4 tokens
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int32_t tb = (x == 0 ? tok0 : tok1) + 4 * kgrp;
-      const bool live = x == 0 || has_b;
+    for (int i = 0; i < 4; ++i) {
+      const int32_t j = tb + i;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int32_t j = tb + i;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const bool vis = live && key_visible(a, j, pos[nt]);
-          s[x][nt][i] = vis ? s[x][nt][i] : -INFINITY;
-        }
-        if (!(live && j < ctx)) vlive[x] &= ~(1u << i);
-      }
+      for (int nt = 0; nt < NT; ++nt) s[nt][i] = key_visible(a, j, pos[nt]) ? s[nt][i] : -INFINITY;
+      const bool data = j < ctx;
+      keep8 |= data ? 0xFFu << (8 * i) : 0u;
+      if (i < 2) keep_lo |= data ? 0xFFFFu << (16 * i) : 0u;
+      else keep_hi |= data ? 0xFFFFu << (16 * (i - 2)) : 0u;
     }
-    sanitize = true;
+#pragma unroll
+    for (int sl = 0; sl < G::SLABS; ++sl)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) r.v[sl][w] &= KV == KV_F16 ? ((w & 1) ? keep_hi : keep_lo) : keep8;
   }
   // ---- online softmax with lazy max refresh
   float mx[NT];
   bool trig = false;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    float v = fmaxf(fmaxf(s[0][nt][0], s[0][nt][1]), fmaxf(s[0][nt][2], s[0][nt][3]));
-    v = fmaxf(v, fmaxf(fmaxf(s[1][nt][0], s[1][nt][1]), fmaxf(s[1][nt][2], s[1][nt][3])));
-    mx[nt] = v;
-    trig |= v > acc.m[nt] + thr;
+    mx[nt] = fmaxf(fmaxf(s[nt][0], s[nt][1]), fmaxf(s[nt][2], s[nt][3]));
+    trig |= mx[nt] > acc.m[nt] + thr;
   }
   if (__any(trig)) {
 #pragma unroll
@@ -175,45 +172,34 @@ __device__ __forceinline__ void compute_pair(Acc<KV, D, NT>& acc, const PairRegs
       rm = fmaxf(rm, __shfl_xor(rm, 16));
       rm = fmaxf(rm, __shfl_xor(rm, 32));
       const bool upd = rm > acc.m[nt] + thr;
-      const float alpha = upd ? (acc.m[nt] == -INFINITY ? 0.0f : exp2f((acc.m[nt] - rm) * c)) : 1.0f;
+      const float alpha = upd ? (acc.m[nt] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((acc.m[nt] - rm) * c))
+                              : 1.0f;
       acc.m[nt] = upd ? rm : acc.m[nt];
       acc.l[nt] *= alpha;
 #pragma unroll
       for (int mt = 0; mt < G::MT; ++mt) acc.o[mt][nt] *= alpha;
     }
   }
-  f16x8 pf[NT];
+  f16x4 pf[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const float mc = acc.m[nt] == -INFINITY ? 0.0f : acc.m[nt] * c;
     float ps = 0.0f;
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e = exp2f(fmaf(s[x][nt][i], c, -mc));
-        ps += e;
-        pf[nt][4 * x + i] = (f16)e;
-      }
+    for (int i = 0; i < 4; ++i) {
+      const float e = __builtin_amdgcn_exp2f(fmaf(s[nt][i], c, -mc));
+      ps += e;
+      pf[nt][i] = (f16)e;
     }
     acc.l[nt] += ps;
   }
   // ---- O^T += V^T . P^T
 #pragma unroll
   for (int mt = 0; mt < G::MT; ++mt) {
-    f16x4 v0 = v_quad<KV, D>(r, 0, mt);
-    f16x4 v1 = v_quad<KV, D>(r, 1, mt);
-    if (sanitize) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v0[i] = (vlive[0] >> i) & 1u ? v0[i] : (f16)0.0f;
-        v1[i] = (vlive[1] >> i) & 1u ? v1[i] : (f16)0.0f;
-      }
-    }
-    const f16x8 vop = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    const f16x4 vop = v_operand<KV, D>(r, mt);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
-      acc.o[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pf[nt], acc.o[mt][nt], 0, 0, 0);
+      acc.o[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(vop, pf[nt], acc.o[mt][nt], 0, 0, 0);
   }
 }
 
@@ -221,7 +207,8 @@ template <int KV, int D, int NT>
 __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
   using G = Geo<KV, D>;
   __shared__ float sm_ml[2][kWaves][NT * 16];
-  __shared__ f32x4 sm_o[2][G::MT * NT][kWave];
+  __shared__ f32x4 sm_o[kWaves / 2][G::MT * NT][kWave];
+  __shared__ f16x8 sm_q[NT][G::KS][kWave];
 
   UnitId u;
   if (!decode_unit(a, row_groups, u)) return;
@@ -251,35 +238,50 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a,
     pg = unit_pages(a, ctx, q_len, lo, hi);
   }
   const int32_t npages = pg.count();
-  const int32_t npairs = (npages + 1) / 2;
   const int32_t* bt_row = a.block_tables + (int64_t)u.b * a.bt_stride;
 
   // query fragments: lane (kgrp, ncol) holds row ncol of each 16-row tile,
-  // dims kgrp * D/4 + 8 * ks .. + 8
-  f16x8 qf[NT][G::KS];
+  // dims kgrp * D/4 + 8 * ks .. + 8.  They are the same for the 4 waves, so
+  // wave 0 converts them once into LDS and every wave reads them per pair
+  // (keeping registers for the load pipeline).
   int32_t pos[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int32_t r = row0 + nt * 16 + ncol;
-    const bool live = r < rows && !bad;
-    const int32_t qi = live ? r / g : 0;
-    const int32_t hj = live ? r % g : 0;
-    pos[nt] = live ? ctx - q_len + qi : ctx - 1;
-    const int64_t qbase = (((int64_t)(q0 + qi) * a.hq + u.h * g + hj) * D) + kgrp * (D / 4);
+    pos[nt] = (r < rows && !bad) ? ctx - q_len + r / g : ctx - 1;
+  }
+  if (wave == 0) {
+    u32x4 qraw[NT][G::KS];
+    bool qlive[NT];
 #pragma unroll
-    for (int ks = 0; ks < G::KS; ++ks) {
-      if (!live) { qf[nt][ks] = f16x8{0, 0, 0, 0, 0, 0, 0, 0}; continue; }
-      const u32x4 w = load16(reinterpret_cast<const uint16_t*>(a.q) + qbase + 8 * ks);
-      if (a.q_bf16) {
+    for (int nt = 0; nt < NT; ++nt) {
+      const int32_t r = row0 + nt * 16 + ncol;
+      qlive[nt] = r < rows && !bad;
+      const int64_t qrow = qlive[nt] ? ((int64_t)(q0 + r / g) * a.hq + u.h * g + r % g) : 0;
+      const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + qrow * D + kgrp * (D / 4);
+#pragma unroll
+      for (int ks = 0; ks < G::KS; ++ks) qraw[nt][ks] = load16(qp + 8 * ks);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+      for (int ks = 0; ks < G::KS; ++ks) {
+        const u32x4 w = qlive[nt] ? qraw[nt][ks] : u32x4{0, 0, 0, 0};
         f16x8 h;
+        if (a.q_bf16) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) h[i] = (f16)bf16_to_f32((uint16_t)(w[i >> 1] >> (16 * (i & 1))));
-        qf[nt][ks] = h;
-      } else {
-        qf[nt][ks] = as<f16x8>(w);
+          for (int i = 0; i < 8; ++i) {
+            const uint32_t word = w[i >> 1];
+            h[i] = (f16)bf16_to_f32((uint16_t)(word >> (16 * (i & 1))));
+          }
+        } else {
+          h = as<f16x8>(w);
+        }
+        sm_q[nt][ks][lane] = h;
       }
     }
   }
+  __syncthreads();
 
   Acc<KV, D, NT> acc;
 #pragma unroll
@@ -293,16 +295,32 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a,
   const float thr = kLazy / c;
   const uint32_t lane_off = (uint32_t)lane * 16u;
 
-  // ---- main loop: two register buffers, the next pair loads while one computes
-  PairRegs<KV, D> ra{}, rb{};   // zeroed: no path carries undefined registers into the loop
-  int32_t p = wave;
-  if (p < npairs) load_pair<KV, D>(ra, a, pg, npages, p, bt_row, u.h, lane_off, bad);
-  for (; p < npairs; p += 2 * kWaves) {
-    if (p + kWaves < npairs) load_pair<KV, D>(rb, a, pg, npages, p + kWaves, bt_row, u.h, lane_off, bad);
-    compute_pair<KV, D, NT>(acc, ra, qf, a, pg, npages, p, ctx, q_len, pos, kgrp, c, thr);
-    if (p + kWaves >= npairs) break;
-    if (p + 2 * kWaves < npairs) load_pair<KV, D>(ra, a, pg, npages, p + 2 * kWaves, bt_row, u.h, lane_off, bad);
-    compute_pair<KV, D, NT>(acc, rb, qf, a, pg, npages, p + kWaves, ctx, q_len, pos, kgrp, c, thr);
+  // ---- main loop over the wave's pages (page wave + 4 i) through a ring of
+  // NBUF register buffers: the loads of pages i + 1 .. i + NBUF - 1 are in
+  // flight while page i computes.
+  PageIdChunks ids;
+  init_ids<1, kWaves>(ids, pg, npages, bt_row, wave, lane);
+  const int32_t my_pages = npages > wave ? (npages - wave + kWaves - 1) / kWaves : 0;
+  if (my_pages > 0) {
+    constexpr int NB = G::NBUF;
+    PageRegs<KV, D> buf[NB];
+#pragma unroll
+    for (int j = 0; j < NB - 1; ++j)
+      load_page<KV, D>(buf[j], ids, a, pg, npages, wave, j, bt_row, u.h, lane_off, lane, bad);
+    for (int32_t i = 0;; i += NB) {
+      bool done = false;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        if (!done) {
+          load_page<KV, D>(buf[(j + NB - 1) % NB], ids, a, pg, npages, wave, i + j + NB - 1, bt_row, u.h,
+                           lane_off, lane, bad);
+          compute_page<KV, D, NT>(acc, buf[j], sm_q, lane, a, pg, wave + kWaves * (i + j), ctx, q_len, pos,
+                                  kgrp, c, thr);
+          done = i + j + 1 >= my_pages;
+        }
+      }
+      if (done) break;
+    }
   }
 
   // ---- combine the waves: rows' (m, l), then O in a fixed tree order
@@ -338,34 +356,26 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a,
 #pragma unroll
     for (int mt = 0; mt < G::MT; ++mt) acc.o[mt][nt] *= fself;
   }
-  // round 1: waves 2, 3 -> waves 0, 1
-  if (wave >= 2) {
+  // fixed-order tree: in each round the upper half of the live waves hands its
+  // O to the lower half through LDS ((O0 + O4) + (O2 + O6)) + ((O1 + O5) + (O3 + O7))
 #pragma unroll
-    for (int mt = 0; mt < G::MT; ++mt)
+  for (int half = kWaves / 2; half >= 1; half /= 2) {
+    if (wave >= half && wave < 2 * half) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) sm_o[wave - 2][mt * NT + nt][lane] = acc.o[mt][nt];
+      for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) sm_o[wave - half][mt * NT + nt][lane] = acc.o[mt][nt];
+    }
+    __syncthreads();
+    if (wave < half) {
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc.o[mt][nt] += sm_o[wave][mt * NT + nt][lane];
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  if (wave < 2) {
-#pragma unroll
-    for (int mt = 0; mt < G::MT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc.o[mt][nt] += sm_o[wave][mt * NT + nt][lane];
-  }
-  __syncthreads();
-  // round 2: wave 1 -> wave 0
-  if (wave == 1) {
-#pragma unroll
-    for (int mt = 0; mt < G::MT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) sm_o[0][mt * NT + nt][lane] = acc.o[mt][nt];
-  }
-  __syncthreads();
   if (wave != 0) return;
-#pragma unroll
-  for (int mt = 0; mt < G::MT; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc.o[mt][nt] += sm_o[0][mt * NT + nt][lane];
 
   // ---- epilogue: lane writes row (nt, ncol), dims (4*kgrp+i)*MT .. +MT
   const float vs = a.v_scale;

@@ -39,28 +39,22 @@ struct PageRegs {
   u32x4 v[VGeo<KV, D>::SLABS];
 };
 
+// Issue the loads of the wave's i-th page (page wave + 4 i of the unit).
+// Branch-free: a page past the unit's end loads page 0 and is masked later.
 template <int KV, int D>
-__device__ __forceinline__ void load_page(PageRegs<KV, D>& r, const AttnLaunch& a, const UnitPages& pg,
-                                          int32_t npages, int32_t n, const int32_t* bt_row, int h,
-                                          uint32_t lane_off, bool& bad) {
+__device__ __forceinline__ void load_page(PageRegs<KV, D>& r, PageIdChunks& ids, const AttnLaunch& a,
+                                          const UnitPages& pg, int32_t npages, int32_t wave, int32_t i,
+                                          const int32_t* bt_row, int h, uint32_t lane_off, int lane, bool& bad) {
   using G = VGeo<KV, D>;
-  int32_t pid = -1;
-  if (n < npages) {
-    pid = bt_row[pg.page(n)];
-    if (pid < 0 || pid >= a.num_pages) { bad = true; pid = -1; }
-  }
-  if (pid >= 0) {
-    const int64_t blk = ((int64_t)pid * a.hkv + h) * G::BLK;
-    const uint8_t* kp = a.k_cache + blk + lane_off;
-    const uint8_t* vp = a.v_cache + blk + lane_off;
+  const bool live = wave_page<1, kWaves>(wave, i) < npages;
+  const int32_t pid = page_id<1, kWaves>(ids, a, pg, npages, bt_row, wave, i, lane, live, bad);
+  const int64_t blk = ((int64_t)pid * a.hkv + h) * G::BLK;
+  const uint8_t* kp = a.k_cache + blk + lane_off;
+  const uint8_t* vp = a.v_cache + blk + lane_off;
 #pragma unroll
-    for (int j = 0; j < G::SLABS; ++j) r.k[j] = load16(kp + j * 1024);
+  for (int j = 0; j < G::SLABS; ++j) r.k[j] = load16(kp + j * 1024);
 #pragma unroll
-    for (int j = 0; j < G::SLABS; ++j) r.v[j] = load16(vp + j * 1024);
-  } else {
-#pragma unroll
-    for (int j = 0; j < G::SLABS; ++j) { r.k[j] = u32x4{0, 0, 0, 0}; r.v[j] = u32x4{0, 0, 0, 0}; }
-  }
+  for (int j = 0; j < G::SLABS; ++j) r.v[j] = load16(vp + j * 1024);
 }
 
 // The lane's K dims as fp16 pairs (QD / 2 words).
@@ -101,7 +95,7 @@ struct VAcc {
 };
 
 template <int KV, int D, int RP>
-__device__ __forceinline__ void compute_page(VAcc<D, RP>& acc, const PageRegs<KV, D>& r,
+__device__ __forceinline__ void compute_page(VAcc<D, RP>& acc, PageRegs<KV, D>& r,
                                              const f16x2 (&qh)[RP][VGeo<KV, D>::QD / 2],
                                              const AttnLaunch& a, const UnitPages& pg, int32_t npages,
                                              int32_t n, int32_t ctx, int32_t q_len, const int32_t (&pos)[RP],
@@ -127,7 +121,7 @@ __device__ __forceinline__ void compute_page(VAcc<D, RP>& acc, const PageRegs<KV
   }
   const int32_t tok0 = pg.page(n) * kPage;
   const bool need_mask = (tok0 + kPage - 1 > ctx - q_len) ||
-                         (a.window >= 0 && tok0 <= ctx - q_len - a.window);
+                         (a.window >= 0 && tok0 <= ctx - 1 - a.window);
   if (need_mask) {
     const int32_t j = tok0 + t;
 #pragma unroll
@@ -146,7 +140,7 @@ __device__ __forceinline__ void compute_page(VAcc<D, RP>& acc, const PageRegs<KV
       rm = fmaxf(rm, __shfl_xor(rm, 4));
       rm = fmaxf(rm, __shfl_xor(rm, 8));
       const bool upd = rm > acc.m[rr] + thr;
-      const float alpha = upd ? (acc.m[rr] == -INFINITY ? 0.0f : exp2f((acc.m[rr] - rm) * c)) : 1.0f;
+      const float alpha = upd ? (acc.m[rr] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((acc.m[rr] - rm) * c)) : 1.0f;
       acc.m[rr] = upd ? rm : acc.m[rr];
       acc.l[rr] *= alpha;
 #pragma unroll
@@ -157,7 +151,7 @@ __device__ __forceinline__ void compute_page(VAcc<D, RP>& acc, const PageRegs<KV
 #pragma unroll
   for (int rr = 0; rr < RP; ++rr) {
     const float mc = acc.m[rr] == -INFINITY ? 0.0f : acc.m[rr] * c;
-    p[rr] = exp2f(fmaf(s[rr], c, -mc));
+    p[rr] = __builtin_amdgcn_exp2f(fmaf(s[rr], c, -mc));
     acc.l[rr] += p[rr];       // every lane group holds the same p; group 0's sum is used
   }
   // ---- exchange p through LDS: sm_p[row][token]
@@ -166,19 +160,28 @@ __device__ __forceinline__ void compute_page(VAcc<D, RP>& acc, const PageRegs<KV
     for (int rr = 0; rr < RP; ++rr) sm_p[rr * 16 + t] = p[rr];
   }
   __builtin_amdgcn_wave_barrier();      // LDS requests of one wave complete in order
-  // tokens 4kq .. 4kq+3 beyond ctx carry stale data: zero their V
+  // tokens 4kq .. 4kq+3 beyond ctx carry stale data: zero their V codes
   const int32_t jq = tok0 + 4 * kq;
-  const bool tail = jq + 3 >= ctx;
+  if (jq + 3 >= ctx) {
+    uint32_t keep8 = 0, keep_lo = 0, keep_hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool data = jq + i < ctx;
+      keep8 |= data ? 0xFFu << (8 * i) : 0u;
+      if (i < 2) keep_lo |= data ? 0xFFFFu << (16 * i) : 0u;
+      else keep_hi |= data ? 0xFFFFu << (16 * (i - 2)) : 0u;
+    }
+#pragma unroll
+    for (int sl = 0; sl < G::SLABS; ++sl)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) r.v[sl][w] &= KV == KV_F16 ? ((w & 1) ? keep_hi : keep_lo) : keep8;
+  }
   f32x4 pr[RP];
 #pragma unroll
   for (int rr = 0; rr < RP; ++rr) pr[rr] = *reinterpret_cast<const f32x4*>(sm_p + rr * 16 + 4 * kq);
 #pragma unroll
   for (int mt = 0; mt < G::MT; ++mt) {
-    f16x4 v = v_quad_vec<KV, D>(r, mt);
-    if (tail) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = jq + i < ctx ? v[i] : (f16)0.0f;
-    }
+    const f16x4 v = v_quad_vec<KV, D>(r, mt);
 #pragma unroll
     for (int rr = 0; rr < RP; ++rr) {
       float x = acc.o[rr][mt];
@@ -227,27 +230,35 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_vec_kernel(AttnLaunch a, 
   const int32_t npages = pg.count();
   const int32_t* bt_row = a.block_tables + (int64_t)u.b * a.bt_stride;
 
-  // queries: row rr, the lane's K dims kgrp * D/4 .. + D/4, as fp16 pairs
+  // queries: row rr, the lane's K dims kgrp * D/4 .. + D/4, as fp16 pairs.
+  // All loads are issued before any is used.
   f16x2 qh[RP][G::QD / 2];
+  u32x4 qraw[RP][G::QD / 8];
+  bool qlive[RP];
   int32_t pos[RP];
 #pragma unroll
   for (int rr = 0; rr < RP; ++rr) {
     const int32_t r = row0 + rr;
-    const bool live = r < rows && !bad;
-    const int32_t qi = live ? r / g : 0, hj = live ? r % g : 0;
-    pos[rr] = live ? ctx - q_len + qi : ctx - 1;
-    const int64_t qbase = (((int64_t)(q0 + qi) * a.hq + u.h * g + hj) * D) + kgrp * G::QD;
+    qlive[rr] = r < rows && !bad;
+    pos[rr] = qlive[rr] ? ctx - q_len + r / g : ctx - 1;
+    const int64_t qrow = qlive[rr] ? ((int64_t)(q0 + r / g) * a.hq + u.h * g + r % g) : 0;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + qrow * D + kgrp * G::QD;
+#pragma unroll
+    for (int w = 0; w < G::QD / 8; ++w) qraw[rr][w] = load16(qp + 8 * w);
+  }
+#pragma unroll
+  for (int rr = 0; rr < RP; ++rr) {
 #pragma unroll
     for (int w = 0; w < G::QD / 8; ++w) {
-      u32x4 x = u32x4{0, 0, 0, 0};
-      if (live) x = load16(reinterpret_cast<const uint16_t*>(a.q) + qbase + 8 * w);
+      const u32x4 x = qlive[rr] ? qraw[rr][w] : u32x4{0, 0, 0, 0};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        const uint32_t word = x[i];
         if (a.q_bf16) {
-          qh[rr][4 * w + i] = f16x2{(f16)bf16_to_f32((uint16_t)(x[i] & 0xFFFFu)),
-                                    (f16)bf16_to_f32((uint16_t)(x[i] >> 16))};
+          qh[rr][4 * w + i] = f16x2{(f16)bf16_to_f32((uint16_t)(word & 0xFFFFu)),
+                                    (f16)bf16_to_f32((uint16_t)(word >> 16))};
         } else {
-          qh[rr][4 * w + i] = as<f16x2>(x[i]);
+          qh[rr][4 * w + i] = as<f16x2>(word);
         }
       }
     }
@@ -266,15 +277,23 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_vec_kernel(AttnLaunch a, 
   const uint32_t lane_off = (uint32_t)lane * 16u;
   float* smp = sm_p[wave];
 
-  PageRegs<KV, D> ra{}, rb{};   // zeroed: no path carries undefined registers into the loop
-  int32_t n = wave;
-  if (n < npages) load_page<KV, D>(ra, a, pg, npages, n, bt_row, u.h, lane_off, bad);
-  for (; n < npages; n += 2 * kWaves) {
-    if (n + kWaves < npages) load_page<KV, D>(rb, a, pg, npages, n + kWaves, bt_row, u.h, lane_off, bad);
-    compute_page<KV, D, RP>(acc, ra, qh, a, pg, npages, n, ctx, q_len, pos, lane, c, thr, smp);
-    if (n + kWaves >= npages) break;
-    if (n + 2 * kWaves < npages) load_page<KV, D>(ra, a, pg, npages, n + 2 * kWaves, bt_row, u.h, lane_off, bad);
-    compute_page<KV, D, RP>(acc, rb, qh, a, pg, npages, n + kWaves, ctx, q_len, pos, lane, c, thr, smp);
+  // main loop over the wave's pages (page wave + 4 i): two register buffers,
+  // the next page's loads are in flight while one page computes
+  PageIdChunks ids;
+  init_ids<1, kWaves>(ids, pg, npages, bt_row, wave, lane);
+  const int32_t my_pages = npages > wave ? (npages - wave + kWaves - 1) / kWaves : 0;
+  if (my_pages > 0) {
+    PageRegs<KV, D> ra, rb;
+    load_page<KV, D>(ra, ids, a, pg, npages, wave, 0, bt_row, u.h, lane_off, lane, bad);
+    for (int32_t i = 0;; i += 2) {
+      load_page<KV, D>(rb, ids, a, pg, npages, wave, i + 1, bt_row, u.h, lane_off, lane, bad);
+      compute_page<KV, D, RP>(acc, ra, qh, a, pg, npages, wave + kWaves * i, ctx, q_len, pos, lane, c, thr, smp);
+      if (i + 1 >= my_pages) break;
+      load_page<KV, D>(ra, ids, a, pg, npages, wave, i + 2, bt_row, u.h, lane_off, lane, bad);
+      compute_page<KV, D, RP>(acc, rb, qh, a, pg, npages, wave + kWaves * (i + 1), ctx, q_len, pos, lane, c, thr,
+                              smp);
+      if (i + 2 >= my_pages) break;
+    }
   }
 
   // ---- per wave: sum o over the 4 token quads, l over the 16 tokens

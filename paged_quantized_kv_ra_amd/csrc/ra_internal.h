@@ -86,7 +86,7 @@ constexpr int kVecRowsPerBlock = 8;
 
 // Automatic partition sizes (tokens), constants of the library.
 constexpr int kAutoPartMfma = 2048;
-constexpr int kAutoPartVec = 1024;
+constexpr int kAutoPartVec = 256;
 
 hipError_t launch_attn_mfma(const AttnLaunch& a, hipStream_t s);
 hipError_t launch_attn_vec(const AttnLaunch& a, hipStream_t s);

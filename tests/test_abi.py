@@ -172,9 +172,9 @@ def test_fp16_cache_ignores_scales_and_workspace_query():
     assert slots == 3 and po == 3 * 10 * 16 * 128 and pl == 3 * 10 * 16
     a = _good_args(L, num_splits=64, block_table_stride=1000, max_context_len=16000)
     assert L.paged_attn_workspace(a)[0] == 64
-    # decode rows (g * q_len < 16) use the vector kernel's 1024-token partitions
+    # decode rows (g * q_len < 16) use the vector kernel's 256-token partitions
     a = _good_args(L, num_splits=0, max_q_len=1, min_q_len=1, block_table_stride=1000, max_context_len=5000)
-    assert L.paged_attn_workspace(a)[0] == 5
+    assert L.paged_attn_workspace(a)[0] == 20
 
 
 def test_empty_batch_is_ok_without_pointers():

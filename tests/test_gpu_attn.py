@@ -32,6 +32,11 @@ CASES = [
     ("mfma_g8_q16_window_nosink", [1000, 600], 16, 16, 2, 128, "e4m3", "f16", 33, 0, 1),
     ("mfma_g6_q4_d128_f16", [129, 400], 4, 12, 2, 128, "f16", "f16", -1, 0, 3),
     ("mixed_paths", [500, 400, 300, 64], [1, 5, 2, 16], 16, 2, 128, "e4m3", "f16", -1, 0, 0),
+    # window edges that fall inside pages for the later queries of the block
+    ("mfma_g8_q16_window37_direct", [1000, 333, 70], 16, 16, 2, 128, "e4m3", "f16", 37, 0, 1),
+    ("mfma_g8_q7_window100_sink20", [1000, 517], 7, 16, 2, 128, "int8", "f16", 100, 20, 1),
+    ("mfma_g8_q5_window250_auto", [3000, 260], 5, 16, 2, 128, "f16", "f16", 250, 4, 0),
+    ("vec_g4_q3_window45", [700, 90], 3, 8, 2, 128, "e4m3", "f16", 45, 2, 1),
 ]
 
 
