@@ -26,16 +26,14 @@ namespace ra {
 namespace {
 
 constexpr int kWaves = 8;   // waves per workgroup (two per SIMD)
+constexpr int kSlab = 1024; // bytes of one wavefront-wide 16-byte load
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;   // log2 headroom before the running max is refreshed
 
-// depth of the per-wave page ring (tuning constants)
-#ifndef RA_MFMA_RING_8BIT
-#define RA_MFMA_RING_8BIT 2
-#endif
-#ifndef RA_MFMA_RING_16BIT
-#define RA_MFMA_RING_16BIT 2
+#ifndef RA_MFMA_RING_KIB
+#define RA_MFMA_RING_KIB 8
 #endif
 
 template <int KV, int D>
@@ -45,8 +43,11 @@ struct Geo {
   static constexpr int KS = D / 32;              // k-steps of the QK product
   static constexpr int MT = D / 16;              // 16-dim tiles of the PV product
   static constexpr int BLK = kPage * D * E;      // bytes per (page, head) block
-  // register buffers of the page ring: one page (K and V) is 8 * SLABS VGPRs
-  static constexpr int NBUF = E == 1 ? RA_MFMA_RING_8BIT : RA_MFMA_RING_16BIT;
+  static constexpr int NSL = 2 * SLABS;          // 1 KiB slabs per page (K, then V)
+  // depth of the per-wave LDS page ring: RA_MFMA_RING_KIB of LDS per wave,
+  // 2 .. 8 pages; NRING - 1 pages are in flight while one computes
+  static constexpr int NRING_RAW = RA_MFMA_RING_KIB / NSL;
+  static constexpr int NRING = NRING_RAW > 8 ? 8 : (NRING_RAW < 2 ? 2 : NRING_RAW);
 };
 
 template <int KV, int D>
@@ -55,23 +56,84 @@ struct PageRegs {
   u32x4 v[Geo<KV, D>::SLABS];
 };
 
-// Issue the loads of the wave's i-th page (logical page wave + 4 i of the
-// unit).  Branch-free: a page past the unit's end loads page 0 and is never
-// computed, so the compiler can keep the next pages' loads in flight.
+// Page ids of the pages one wave visits, staged 64 at a time in LDS by the
+// same DMA path as the pages, so that the wave's vector-memory counter only
+// tracks loads whose order the ring accounts for.  Lane j of chunk c holds the
+// raw block-table entry of the wave's (64 c + j)-th page (logical page
+// wave + 8 (64 c + j)); chunk c + 1 is requested when chunk c is taken up.
+struct IdRing {
+  int32_t cur;     // per-lane ids of chunk `chunk`
+  int32_t chunk;
+};
+
+__device__ __forceinline__ void id_dma(int32_t* slot, const UnitPages& pg, int32_t npages, const int32_t* bt_row,
+                                       int32_t wave, int32_t chunk, int lane) {
+  const int32_t n = wave + kWaves * (chunk * 64 + lane);
+  if (n < npages) __builtin_amdgcn_global_load_lds(bt_row + pg.page(n), (lds_u8*)slot, 4, 0, 0);
+}
+
+// Checked physical id of the wave's k-th page (k non-decreasing).  On entry to
+// a new chunk its DMA must have retired: the caller waits for every load older
+// than the last NRING - 1 pages, and a chunk is requested 64 pages before use.
+// An id outside [0, num_pages) makes the unit bad and reads page 0 instead.
+__device__ __forceinline__ int32_t ring_page_id(IdRing& r, int32_t (*sm_id)[64], const AttnLaunch& a,
+                                                const UnitPages& pg, int32_t npages, const int32_t* bt_row,
+                                                int32_t wave, int32_t k, int lane, bool& bad) {
+  const int32_t ch = k >> 6;
+  if (ch != r.chunk) {       // wave-uniform, once per 64 pages
+    r.chunk = ch;
+    r.cur = sm_id[ch & 1][lane];
+    id_dma(sm_id[(ch + 1) & 1], pg, npages, bt_row, wave, ch + 1, lane);
+  }
+  int32_t id = __builtin_amdgcn_readlane(r.cur, k & 63);
+  if (id < 0 || id >= a.num_pages) {
+    bad = true;
+    id = 0;
+  }
+  return id;
+}
+
+// Issue the loads of the wave's i-th page (i < the wave's page count)
+// straight into the LDS ring slot `ring`: one global_load_lds_dwordx4 per 1 KiB
+// slab, lane L writing bytes L*16 .. L*16+15 of the slab, the lane order the
+// cache layout has in HBM.
 template <int KV, int D>
-__device__ __forceinline__ void load_page(PageRegs<KV, D>& r, PageIdChunks& ids, const AttnLaunch& a,
-                                          const UnitPages& pg, int32_t npages, int32_t wave, int32_t i,
-                                          const int32_t* bt_row, int h, uint32_t lane_off, int lane, bool& bad) {
+__device__ __forceinline__ void issue_page(uint8_t (*ring)[kSlab], IdRing& ids, int32_t (*sm_id)[64],
+                                           const AttnLaunch& a, const UnitPages& pg, int32_t npages, int32_t wave,
+                                           int32_t i, const int32_t* bt_row, int h, int lane, bool& bad) {
   using G = Geo<KV, D>;
-  const bool live = wave_page<1, kWaves>(wave, i) < npages;
-  const int32_t pid = page_id<1, kWaves>(ids, a, pg, npages, bt_row, wave, i, lane, live, bad);
+  const int32_t pid = ring_page_id(ids, sm_id, a, pg, npages, bt_row, wave, i, lane, bad);
   const int64_t blk = ((int64_t)pid * a.hkv + h) * G::BLK;
-  const uint8_t* kp = a.k_cache + blk + lane_off;
-  const uint8_t* vp = a.v_cache + blk + lane_off;
+  const uint8_t* kp = a.k_cache + blk + (uint32_t)lane * 16u;
+  const uint8_t* vp = a.v_cache + blk + (uint32_t)lane * 16u;
 #pragma unroll
-  for (int j = 0; j < G::SLABS; ++j) r.k[j] = load16(kp + j * 1024);
+  for (int j = 0; j < G::SLABS; ++j) __builtin_amdgcn_global_load_lds(kp + j * kSlab, (lds_u8*)ring[j], 16, 0, 0);
 #pragma unroll
-  for (int j = 0; j < G::SLABS; ++j) r.v[j] = load16(vp + j * 1024);
+  for (int j = 0; j < G::SLABS; ++j)
+    __builtin_amdgcn_global_load_lds(vp + j * kSlab, (lds_u8*)ring[G::SLABS + j], 16, 0, 0);
+}
+
+// Wait until at most `n` of this wave's vector-memory operations are
+// outstanding (the LDS ring's loads retire in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14;
+  // expcnt (bits 6:4) and lgkmcnt (bits 11:8) left at their maxima
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt at their maxima
+}
+
+template <int KV, int D>
+__device__ __forceinline__ void read_page(PageRegs<KV, D>& r, const uint8_t (*ring)[kSlab], uint32_t lane_off) {
+  using G = Geo<KV, D>;
+#pragma unroll
+  for (int j = 0; j < G::SLABS; ++j) r.k[j] = *reinterpret_cast<const u32x4*>(ring[j] + lane_off);
+#pragma unroll
+  for (int j = 0; j < G::SLABS; ++j) r.v[j] = *reinterpret_cast<const u32x4*>(ring[G::SLABS + j] + lane_off);
 }
 
 // K operand of k-step ks: the lane's token, dims kgrp * D/4 + 8 ks .. + 8.
@@ -114,7 +176,7 @@ struct Acc {
 
 template <int KV, int D, int NT>
 __device__ __forceinline__ void compute_page(Acc<KV, D, NT>& acc, PageRegs<KV, D>& r,
-                                             const f16x8 (*sm_q)[Geo<KV, D>::KS][kWave], int lane,
+                                             const f16x8 (&qf)[NT][Geo<KV, D>::KS],
                                              const AttnLaunch& a, const UnitPages& pg, int32_t n, int32_t ctx,
                                              int32_t q_len, const int32_t (&pos)[NT], int kgrp, float c,
                                              float thr) {
@@ -123,16 +185,12 @@ __device__ __forceinline__ void compute_page(Acc<KV, D, NT>& acc, PageRegs<KV, D
   f32x4 s[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) s[nt] = f32x4{0, 0, 0, 0};
-  // the query fragments are re-read from LDS for every page (an opaque index
-  // keeps the compiler from hoisting them into registers for the whole loop)
-  int li = lane;
-  asm volatile("" : "+v"(li));
 #pragma unroll
   for (int ks = 0; ks < G::KS; ++ks) {
     const f16x8 kop = k_operand<KV, D>(r, ks);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
-      s[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, sm_q[nt][ks][li], s[nt], 0, 0, 0);
+      s[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qf[nt][ks], s[nt], 0, 0, 0);
   }
   // ---- masks (only on pages that can hold an invisible key).  Keys past ctx
   // (stale bytes of the last page) also get their V codes zeroed so that
@@ -206,9 +264,16 @@ __device__ __forceinline__ void compute_page(Acc<KV, D, NT>& acc, PageRegs<KV, D
 template <int KV, int D, int NT>
 __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
   using G = Geo<KV, D>;
+  // LDS: the per-wave page rings, reused for the cross-wave merge of O
+  constexpr int kRingBytes = kWaves * G::NRING * G::NSL * kSlab;
+  // merge buffer: per pass, (nt, i) pairs x waves x lanes x MT floats
+  constexpr int kPairs = 2 * NT;
+  constexpr int kMergeBytes = kPairs * kWaves * kWave * G::MT * 4;
+  constexpr int kRawBytes = kRingBytes > kMergeBytes ? kRingBytes : kMergeBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t sm_raw[kRawBytes / kSlab][kSlab];
   __shared__ float sm_ml[2][kWaves][NT * 16];
-  __shared__ f32x4 sm_o[kWaves / 2][G::MT * NT][kWave];
-  __shared__ f16x8 sm_q[NT][G::KS][kWave];
+  __shared__ int32_t sm_ids[kWaves][2][64];
+  __shared__ int32_t sm_bad[kWaves];
 
   UnitId u;
   if (!decode_unit(a, row_groups, u)) return;
@@ -240,48 +305,46 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a,
   const int32_t npages = pg.count();
   const int32_t* bt_row = a.block_tables + (int64_t)u.b * a.bt_stride;
 
+  // first two chunks of the wave's page ids (DMA into LDS)
+  int32_t (*sm_id)[64] = sm_ids[wave];
+  id_dma(sm_id[0], pg, npages, bt_row, wave, 0, lane);
+  id_dma(sm_id[1], pg, npages, bt_row, wave, 1, lane);
+  const uint32_t lane_off = (uint32_t)lane * 16u;
+
   // query fragments: lane (kgrp, ncol) holds row ncol of each 16-row tile,
-  // dims kgrp * D/4 + 8 * ks .. + 8.  They are the same for the 4 waves, so
-  // wave 0 converts them once into LDS and every wave reads them per pair
-  // (keeping registers for the load pipeline).
+  // dims kgrp * D/4 + 8 * ks .. + 8.  Every wave loads its own copy, in
+  // flight together with the id DMA, and keeps it in registers.
   int32_t pos[NT];
+  u32x4 qraw[NT][G::KS];
+  bool qlive[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int32_t r = row0 + nt * 16 + ncol;
-    pos[nt] = (r < rows && !bad) ? ctx - q_len + r / g : ctx - 1;
+    qlive[nt] = r < rows && !bad;
+    pos[nt] = qlive[nt] ? ctx - q_len + r / g : ctx - 1;
+    const int64_t qrow = qlive[nt] ? ((int64_t)(q0 + r / g) * a.hq + u.h * g + r % g) : 0;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + qrow * D + kgrp * (D / 4);
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) qraw[nt][ks] = load16(qp + 8 * ks);
   }
-  if (wave == 0) {
-    u32x4 qraw[NT][G::KS];
-    bool qlive[NT];
+  wait_vmcnt<0>();   // the first id chunks and the query rows have landed
+  f16x8 qf[NT][G::KS];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int32_t r = row0 + nt * 16 + ncol;
-      qlive[nt] = r < rows && !bad;
-      const int64_t qrow = qlive[nt] ? ((int64_t)(q0 + r / g) * a.hq + u.h * g + r % g) : 0;
-      const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + qrow * D + kgrp * (D / 4);
+  for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-      for (int ks = 0; ks < G::KS; ++ks) qraw[nt][ks] = load16(qp + 8 * ks);
-    }
+    for (int ks = 0; ks < G::KS; ++ks) {
+      const u32x4 w = qlive[nt] ? qraw[nt][ks] : u32x4{0, 0, 0, 0};
+      if (a.q_bf16) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-      for (int ks = 0; ks < G::KS; ++ks) {
-        const u32x4 w = qlive[nt] ? qraw[nt][ks] : u32x4{0, 0, 0, 0};
-        f16x8 h;
-        if (a.q_bf16) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const uint32_t word = w[i >> 1];
-            h[i] = (f16)bf16_to_f32((uint16_t)(word >> (16 * (i & 1))));
-          }
-        } else {
-          h = as<f16x8>(w);
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t word = w[i >> 1];
+          qf[nt][ks][i] = (f16)bf16_to_f32((uint16_t)(word >> (16 * (i & 1))));
         }
-        sm_q[nt][ks][lane] = h;
+      } else {
+        qf[nt][ks] = as<f16x8>(w);
       }
     }
   }
-  __syncthreads();
 
   Acc<KV, D, NT> acc;
 #pragma unroll
@@ -293,141 +356,167 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a,
   }
   const float c = a.softmax_scale * a.k_scale * kLog2e;
   const float thr = kLazy / c;
-  const uint32_t lane_off = (uint32_t)lane * 16u;
 
-  // ---- main loop over the wave's pages (page wave + 4 i) through a ring of
-  // NBUF register buffers: the loads of pages i + 1 .. i + NBUF - 1 are in
-  // flight while page i computes.
-  PageIdChunks ids;
-  init_ids<1, kWaves>(ids, pg, npages, bt_row, wave, lane);
+  // ---- main loop over the wave's pages (page wave + 8 k) through the LDS
+  // ring: page k computes from slot k % NRING while pages k + 1 .. k + NRING - 1
+  // are in flight; once its slab reads have retired, page k + NRING is issued
+  // into the slot it freed.
   const int32_t my_pages = npages > wave ? (npages - wave + kWaves - 1) / kWaves : 0;
   if (my_pages > 0) {
-    constexpr int NB = G::NBUF;
-    PageRegs<KV, D> buf[NB];
+    constexpr int NR = G::NRING;
+    uint8_t (*ring)[kSlab] = &sm_raw[wave * NR * G::NSL];
+    IdRing ids{sm_id[0][lane], 0};
 #pragma unroll
-    for (int j = 0; j < NB - 1; ++j)
-      load_page<KV, D>(buf[j], ids, a, pg, npages, wave, j, bt_row, u.h, lane_off, lane, bad);
-    for (int32_t i = 0;; i += NB) {
-      bool done = false;
+    for (int j = 0; j < NR; ++j)
+      if (j < my_pages)
+        issue_page<KV, D>(ring + j * G::NSL, ids, sm_id, a, pg, npages, wave, j, bt_row, u.h, lane, bad);
+    for (int32_t i = 0; i < my_pages; i += NR) {
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        if (!done) {
-          load_page<KV, D>(buf[(j + NB - 1) % NB], ids, a, pg, npages, wave, i + j + NB - 1, bt_row, u.h,
-                           lane_off, lane, bad);
-          compute_page<KV, D, NT>(acc, buf[j], sm_q, lane, a, pg, wave + kWaves * (i + j), ctx, q_len, pos,
-                                  kgrp, c, thr);
-          done = i + j + 1 >= my_pages;
+      for (int j = 0; j < NR; ++j) {
+        const int32_t k = i + j;
+        if (k < my_pages) {
+          // page k's slabs retire before the (NR - 1) * NSL loads issued after
+          // them, unless the tail issued fewer
+          if (k + NR - 1 < my_pages)
+            wait_vmcnt<(NR - 1) * G::NSL>();
+          else
+            wait_vmcnt<0>();
+          PageRegs<KV, D> r;
+          read_page<KV, D>(r, ring + j * G::NSL, lane_off);
+          compute_page<KV, D, NT>(acc, r, qf, a, pg, wave + kWaves * k, ctx, q_len, pos, kgrp, c, thr);
+          // the slot's reads have returned (their values were consumed) before
+          // the next load may overwrite it
+          wait_lgkmcnt0();
+          if (k + NR < my_pages)
+            issue_page<KV, D>(ring + j * G::NSL, ids, sm_id, a, pg, npages, wave, k + NR, bt_row, u.h, lane, bad);
         }
       }
-      if (done) break;
     }
   }
+  wait_vmcnt<0>();   // no ring load may land after the ring becomes the merge buffer
 
-  // ---- combine the waves: rows' (m, l), then O in a fixed tree order
+  // ---- combine the waves.  Every wave publishes its rows' (m, l) and its
+  // bad flag, then rescales its O to the common row maximum.
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     float l = acc.l[nt];
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
-    acc.l[nt] = l;
     if (kgrp == 0) {
       sm_ml[0][wave][nt * 16 + ncol] = acc.m[nt];
       sm_ml[1][wave][nt * 16 + ncol] = l;
     }
   }
-  bad = __syncthreads_or(bad ? 1 : 0) != 0;
-  float Mrow[NT], Lrow[NT];
+  if (lane == 0) sm_bad[wave] = bad ? 1 : 0;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) bad = bad || sm_bad[w] != 0;
+  float Mrow[NT], Lrow[NT], fself[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int rr = nt * 16 + ncol;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_ml[0][w][rr]);
-    float L = 0.0f, fself = 0.0f;
+    float L = 0.0f;
+    fself[nt] = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float mw = sm_ml[0][w][rr];
-      const float f = (mw == -INFINITY) ? 0.0f : exp2f((mw - M) * c);
+      const float f = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((mw - M) * c);
       L += f * sm_ml[1][w][rr];
-      if (w == wave) fself = f;
+      if (w == wave) fself[nt] = f;
     }
     Mrow[nt] = M;
     Lrow[nt] = L;
-#pragma unroll
-    for (int mt = 0; mt < G::MT; ++mt) acc.o[mt][nt] *= fself;
   }
-  // fixed-order tree: in each round the upper half of the live waves hands its
-  // O to the lower half through LDS ((O0 + O4) + (O2 + O6)) + ((O1 + O5) + (O3 + O7))
-#pragma unroll
-  for (int half = kWaves / 2; half >= 1; half /= 2) {
-    if (wave >= half && wave < 2 * half) {
-#pragma unroll
-      for (int mt = 0; mt < G::MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) sm_o[wave - half][mt * NT + nt][lane] = acc.o[mt][nt];
-    }
-    __syncthreads();
-    if (wave < half) {
-#pragma unroll
-      for (int mt = 0; mt < G::MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc.o[mt][nt] += sm_o[wave][mt * NT + nt][lane];
-    }
-    __syncthreads();
-  }
-  if (wave != 0) return;
 
-  // ---- epilogue: lane writes row (nt, ncol), dims (4*kgrp+i)*MT .. +MT
+  // ---- reduce-scatter of O through LDS, in two passes over the lane's
+  // accumulator components i (pass p: i = 2p, 2p + 1).  The lane's values
+  // acc.o[0..MT)[nt][i] are the MT consecutive dims (4 kgrp + i) * MT .. + MT of
+  // row nt * 16 + ncol; every wave stores them, then wave w < 2 NT sums pair
+  // w = (nt, i) over the waves in wave order and writes that slice of the
+  // output (same lanes, so the row and its (M, L) are the lane's own).
+  float* red = reinterpret_cast<float*>(&sm_raw[0][0]);   // [kPairs][kWaves][kWave][MT]
   const float vs = a.v_scale;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int32_t r = row0 + nt * 16 + ncol;
-    if (r >= rows) continue;
-    const int32_t qi = r / g, hj = r % g;
-    const int64_t orow = (int64_t)(q0 + qi) * a.hq + u.h * g + hj;
-    const float L = Lrow[nt];
-    const float inv = L > 0.0f ? vs / L : 0.0f;
-    float lse = L > 0.0f ? (Mrow[nt] * c + log2f(L)) * kLn2 : -INFINITY;
-    if (bad) lse = __builtin_nanf("");
+  for (int p = 0; p < 2; ++p) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d0 = (4 * kgrp + i) * G::MT;
+    for (int pr = 0; pr < kPairs; ++pr) {
+      const int nt = pr >> 1, i = 2 * p + (pr & 1);
+      float* dst = red + ((pr * kWaves + wave) * kWave + lane) * G::MT;
+#pragma unroll
+      for (int k = 0; k < G::MT / 4; ++k)
+        *reinterpret_cast<f32x4*>(dst + 4 * k) =
+            f32x4{acc.o[4 * k][nt][i], acc.o[4 * k + 1][nt][i], acc.o[4 * k + 2][nt][i], acc.o[4 * k + 3][nt][i]} *
+            fself[nt];
+    }
+    __syncthreads();
+    if (wave < kPairs) {
+      const int pr = wave;
+      const int nt = pr >> 1, i = 2 * p + (pr & 1);
       float v[G::MT];
 #pragma unroll
-      for (int mt = 0; mt < G::MT; ++mt) v[mt] = bad ? __builtin_nanf("") : acc.o[mt][nt][i] * inv;
-      if (a.direct) {
-        uint16_t hv[G::MT];
+      for (int mt = 0; mt < G::MT; ++mt) v[mt] = 0.0f;
 #pragma unroll
-        for (int mt = 0; mt < G::MT; ++mt)
-          hv[mt] = a.q_bf16 ? f32_to_bf16(v[mt]) : as<uint16_t>((f16)v[mt]);
-        uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + orow * D + d0;
+      for (int w = 0; w < kWaves; ++w) {
+        const float* src = red + ((pr * kWaves + w) * kWave + lane) * G::MT;
 #pragma unroll
-        for (int k = 0; k < G::MT / 8; ++k) {
-          u32x4 w;
+        for (int k = 0; k < G::MT / 4; ++k) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(src + 4 * k);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) w[j] = (uint32_t)hv[8 * k + 2 * j] | ((uint32_t)hv[8 * k + 2 * j + 1] << 16);
-          *reinterpret_cast<u32x4*>(op + 8 * k) = w;
+          for (int j = 0; j < 4; ++j) v[4 * k + j] += x[j];
         }
-        if constexpr (G::MT % 8 != 0) {
-          u32x2 w;
-          w[0] = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
-          w[1] = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
-          *reinterpret_cast<u32x2*>(op) = w;
-        }
-      } else {
-        float* op = a.part_out + ((int64_t)u.s * a.total_q * a.hq + orow) * D + d0;
+      }
+      // rows of this pair, by the lane's own (M, L)
+      float L = 0.0f, M = 0.0f;
 #pragma unroll
-        for (int k = 0; k < G::MT / 4; ++k)
-          *reinterpret_cast<f32x4*>(op + 4 * k) = f32x4{v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]};
+      for (int t = 0; t < NT; ++t)
+        if (t == nt) { L = Lrow[t]; M = Mrow[t]; }
+      const int32_t r = row0 + nt * 16 + ncol;
+      if (r < rows) {
+        const int32_t qi = r / g, hj = r % g;
+        const int64_t orow = (int64_t)(q0 + qi) * a.hq + u.h * g + hj;
+        const float inv = L > 0.0f ? vs / L : 0.0f;
+        const int d0 = (4 * kgrp + i) * G::MT;
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt) v[mt] = bad ? __builtin_nanf("") : v[mt] * inv;
+        if (a.direct) {
+          uint16_t hv[G::MT];
+#pragma unroll
+          for (int mt = 0; mt < G::MT; ++mt) hv[mt] = a.q_bf16 ? f32_to_bf16(v[mt]) : as<uint16_t>((f16)v[mt]);
+          uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + orow * D + d0;
+#pragma unroll
+          for (int k = 0; k < G::MT / 8; ++k) {
+            u32x4 w;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) w[j] = (uint32_t)hv[8 * k + 2 * j] | ((uint32_t)hv[8 * k + 2 * j + 1] << 16);
+            *reinterpret_cast<u32x4*>(op + 8 * k) = w;
+          }
+          if constexpr (G::MT % 8 != 0) {
+            u32x2 w;
+            w[0] = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
+            w[1] = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
+            *reinterpret_cast<u32x2*>(op) = w;
+          }
+        } else {
+          float* op = a.part_out + ((int64_t)u.s * a.total_q * a.hq + orow) * D + d0;
+#pragma unroll
+          for (int k = 0; k < G::MT / 4; ++k)
+            *reinterpret_cast<f32x4*>(op + 4 * k) = f32x4{v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]};
+        }
+        if (kgrp == 0 && i == 0) {
+          float lse = L > 0.0f ? (M * c + log2f(L)) * kLn2 : -INFINITY;
+          if (bad) lse = __builtin_nanf("");
+          if (a.direct) {
+            if (a.lse) a.lse[orow] = lse;
+          } else {
+            a.part_lse[(int64_t)u.s * a.total_q * a.hq + orow] = lse;
+          }
+        }
       }
     }
-    if (kgrp == 0) {
-      if (a.direct) {
-        if (a.lse) a.lse[orow] = lse;
-      } else {
-        a.part_lse[(int64_t)u.s * a.total_q * a.hq + orow] = lse;
-      }
-    }
+    if (p == 0) __syncthreads();   // the second pass reuses the buffer
   }
 }
 
