@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every step from the host instead of replaying captured HIP graphs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (for counter scaling)")
     return ap.parse_args()
@@ -137,6 +139,12 @@ class Step:
         import torch
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to("cuda").view(torch.bfloat16)
 
+    def run_attention(self, i, stream):
+        """Enqueue only the attention launch of step i."""
+        st = self.lib.ra_paged_attn(ctypes.byref(self.args[i % self.copies]), ctypes.c_void_p(stream))
+        if st != 0:
+            raise RuntimeError(self.lib.ra_last_error().decode())
+
     def run(self, i, stream, ev=None):
         """Enqueue step i: store, attention (between the two events), merge."""
         w, lib, L = self.w, self.lib, self.L
@@ -205,16 +213,86 @@ def cpu_baseline(w, seconds):
 
 
 def traffic_from_profile(wname, src_hash):
-    """HBM bytes per attention launch from committed rocprofv3 counters, if
-    they were taken on the current kernel sources."""
-    p = os.path.join(ROOT, "profiles", f"attn_traffic_{wname}.json")
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE scaled by a plain copy's reading), if it
+    was taken on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", f"attn_traffic_{wname}.txt")
     if not os.path.exists(p):
         return None
+    fields = {}
     with open(p) as f:
-        d = json.load(f)
-    if d.get("kernel_source_hash") != src_hash:
+        for line in f:
+            k, sep, v = line.partition(":")
+            if sep and k.strip() in ("kernel_source_hash", "hbm_bytes_per_launch"):
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_hash") != src_hash or "hbm_bytes_per_launch" not in fields:
         return None
-    return d.get("hbm_bytes_per_launch")
+    return int(fields["hbm_bytes_per_launch"])
+
+
+def time_graphs(step, args, torch):
+    """Steps replayed from HIP graphs (one per pool copy: store, attention,
+    merge), the way a serving loop launches its decode step.  The attention
+    kernel's average duration is timed separately over back-to-back replays of
+    a graph holding one attention launch per pool copy."""
+    cap = torch.cuda.Stream()
+    step_graphs, attn_graph = [], torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(cap):
+        for c in range(step.copies):          # run once eagerly on the capture stream first
+            step.run(c, cap.cuda_stream)
+    torch.cuda.synchronize()
+    for c in range(step.copies):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            step.run(c, torch.cuda.current_stream().cuda_stream)
+        step_graphs.append(g)
+    with torch.cuda.graph(attn_graph, stream=cap):
+        for c in range(step.copies):
+            step.run_attention(c, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        step_graphs[i % step.copies].replay()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step_graphs[(args.warmup + i) % step.copies].replay()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = start.elapsed_time(stop) / args.steps
+    reps = max(1, args.steps // step.copies)
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record()
+    for _ in range(reps):
+        attn_graph.replay()
+    a1.record()
+    torch.cuda.synchronize()
+    attn_avg_ms = a0.elapsed_time(a1) / (reps * step.copies)
+    return ms_per_step, attn_avg_ms, wall
+
+
+def time_eager(step, args, torch):
+    """Steps launched one by one from the host; the attention launch of every
+    step is bracketed by its own pair of events."""
+    sp = torch.cuda.current_stream().cuda_stream
+    for i in range(args.warmup):
+        step.run(i, sp)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step.run(args.warmup + i, sp, evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    attn_ms = [a.elapsed_time(b) for a, b in evs]
+    return start.elapsed_time(stop) / args.steps, sum(attn_ms) / len(attn_ms), wall
 
 
 def main():
@@ -235,32 +313,18 @@ def main():
     log(f"built {w.name} in {time.time() - t0:.1f}s")
     step = Step(w)
     log(f"pool copies: {step.copies}, partition slots: {step.slots}")
-    stream = torch.cuda.current_stream()
-    sp = stream.cuda_stream
-    for i in range(args.warmup):
-        step.run(i, sp)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    start.record()
-    for i in range(args.steps):
-        step.run(args.warmup + i, sp, evs[i])
-    stop.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = start.elapsed_time(stop)
-    attn_ms = [a.elapsed_time(b) for a, b in evs]
-    attn_avg_ms = sum(attn_ms) / len(attn_ms)
-    ms_per_step = total_ms / args.steps
+    if args.eager:
+        ms_per_step, attn_avg_ms, wall = time_eager(step, args, torch)
+    else:
+        ms_per_step, attn_avg_ms, wall = time_graphs(step, args, torch)
     tokens = w.attended_keys()
     value = tokens / (ms_per_step / 1e3)
     alg = algorithmic_bytes(w)
     achieved = alg / (attn_avg_ms / 1e3) / 1e9
     src_hash = kernel_source_hash()
     traffic = traffic_from_profile(w.name, src_hash)
-    log(f"{args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us/step), "
+    log(f"{args.steps} steps ({'eager' if args.eager else 'graph replay'}): {ms_per_step * 1e3:.1f} us/step "
+        f"(wall {wall / args.steps * 1e6:.1f} us/step), "
         f"attention {attn_avg_ms * 1e3:.1f} us avg, {achieved:.0f} GB/s algorithmic")
     line = {
         "metric": "KV tokens attended/sec and achieved HBM GB/s (% of MI355X peak), FP8 KV @32K",
@@ -278,7 +342,8 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "context": int(w.ctx.max()), "q_len": w.max_q_len,
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "kv_dtype": w.kv_dtype, "page_size": 16, "partition_slots": step.slots,
-                   "kv_pool_copies": step.copies, "parallelism": "single GPU"},
+                   "kv_pool_copies": step.copies, "launch": "eager" if args.eager else "hip_graph",
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "kernel": "attn_mfma_kernel" if w.num_q_heads // w.num_kv_heads

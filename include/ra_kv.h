@@ -111,7 +111,9 @@ enum { RA_KV_F16 = 1, RA_KV_FP8_E4M3 = 2, RA_KV_INT8 = 3 };
  *               aligned, num_pages * num_kv_heads * 16 * head_dim elements each.
  * k_scale, v_scale  (host) per-layer scales; required finite and > 0 for
  *               E4M3 / INT8 (there is no fallback to 1.0), ignored for FP16.
- * head_dim in {64, 128}; page_size must be 16.
+ * head_dim in {64, 128}; page_size must be 16.  One call stores at most
+ * 2^30 / (num_kv_heads * head_dim / 8) tokens (RA_ERR_INVALID_ARG beyond:
+ * store in chunks).
  * Bytes of tokens not stored are left unchanged.
  */
 int32_t ra_kv_store(const void* k, const void* v, int32_t src_dtype,
@@ -203,7 +205,8 @@ int32_t ra_paged_attn_workspace(const ra_attn_args* args, int32_t* slots,
  *
  * partial_out [num_partitions][rows][head_dim] fp32, partial_lse
  * [num_partitions][rows] fp32 (natural log; -inf marks an empty partition,
- * whose out is not read).  For each row: M = max_s lse_s; if M = -inf the
+ * whose out adds nothing whatever it holds, though the buffer is read).  For
+ * each row: M = max_s lse_s; if M = -inf the
  * result is out = 0, lse = -inf; else a_s = exp(lse_s - M),
  * out = sum_s a_s out_s / sum_s a_s, lse = M + ln sum_s a_s, summed in the
  * order s = 0, 1, ...  out [rows][head_dim] of out_dtype (RA_F16, RA_BF16 or

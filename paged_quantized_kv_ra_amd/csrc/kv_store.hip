@@ -22,24 +22,24 @@ template <int KV, int D, bool BF16>
 __global__ void __launch_bounds__(256) kv_store_kernel(StoreLaunch a) {
   constexpr int E = KV == KV_F16 ? 2 : 1;
   constexpr int CH = D / 8;                       // 8-dim chunks per head
-  const int64_t units = a.num_tokens * a.hkv * CH;
+  // the host guarantees num_tokens * hkv * CH < 2^31
+  const int32_t units = (int32_t)(a.num_tokens * a.hkv * CH);
   const int64_t limit = a.num_pages * kPage;
-  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < units;
-       u += (int64_t)gridDim.x * blockDim.x) {
-    const int c = (int)(u % CH);
-    const int64_t th = u / CH;
-    const int h = (int)(th % a.hkv);
-    const int64_t t = th / a.hkv;
-    const int64_t slot = a.slots[t];
-    if (slot < 0 || slot >= limit) continue;
-    const int64_t page = slot >> 4;
-    const int tp = (int)(slot & 15);
+  for (int32_t u = blockIdx.x * blockDim.x + threadIdx.x; u < units; u += gridDim.x * blockDim.x) {
+    const int c = u % CH;
+    const int32_t th = u / CH;
+    const int h = th % a.hkv;
+    const int32_t t = th / a.hkv;
     const int d0 = c * 8;
-
+    // the source rows and the slot are requested together
     const uint16_t* ksrc = reinterpret_cast<const uint16_t*>(a.k) + t * a.k_stride + (int64_t)h * D + d0;
     const uint16_t* vsrc = reinterpret_cast<const uint16_t*>(a.v) + t * a.v_stride + (int64_t)h * D + d0;
     const u32x4 kr = load16(ksrc);
     const u32x4 vr = load16(vsrc);
+    const int64_t slot = a.slots[t];
+    if (slot < 0 || slot >= limit) continue;
+    const int64_t page = slot >> 4;
+    const int tp = (int)(slot & 15);
     float kf[8], vf[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {

@@ -6,12 +6,13 @@
 // normalised; the combination is
 //   M = max_s lse_s,  a_s = exp(lse_s - M),
 //   out = sum_s a_s out_s / sum_s a_s,  lse = M + ln sum_s a_s,
-// summed in the fixed order s = 0, 1, ...  Partitions with lse = -inf are
-// skipped without reading their out.  A NaN lse (a partial whose sequence
+// summed in the fixed order s = 0, 1, ...  Partitions with lse = -inf add
+// nothing, whatever their out holds.  A NaN lse (a partial whose sequence
 // broke a precondition) makes the row NaN.
 //
 // One wavefront per row: lane s holds lse_s for a chunk of 64 partitions, the
-// weights are broadcast with readlane, each lane accumulates D/64 dims.
+// weights are broadcast with a lane shuffle, each lane accumulates D/64 dims;
+// eight partial rows are in flight at a time.
 #include "ra_device.h"
 #include "ra_internal.h"
 
@@ -21,16 +22,41 @@ namespace {
 template <int D, int OUT>
 __global__ void __launch_bounds__(256) lse_merge_kernel(MergeLaunch a) {
   constexpr int PER = D / 64;
+  constexpr int BATCH = 16;                    // partial rows in flight per lane
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= a.rows) return;
   const int lane = threadIdx.x & 63;
+  const float* base_o = a.part_out + row * D + lane * PER;
+  const int64_t pstride = a.rows * D;
 
-  float M = -INFINITY;
-  bool nan = false;
-  for (int s = lane; s < a.parts; s += 64) {
-    const float v = a.part_lse[(int64_t)s * a.rows + row];
-    nan |= !(v == v);
-    M = fmaxf(M, v);
+  // BATCH partial rows are loaded together (a partition of weight 0, with no
+  // visible key, is loaded but adds nothing, whatever its out holds); the
+  // first batch is requested together with the lse values
+  auto load_batch = [&](float (&v)[BATCH][PER], int first, int n) {
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const float* o = base_o + (int64_t)(first + min(j, n - 1)) * pstride;
+      if constexpr (PER == 2) {
+        const float2 x = *reinterpret_cast<const float2*>(o);
+        v[j][0] = x.x;
+        v[j][1] = x.y;
+      } else {
+        v[j][0] = o[0];
+      }
+    }
+  };
+  float v[BATCH][PER];
+  load_batch(v, 0, min(a.parts, 64));
+
+  // lane s holds lse_s of the first 64 partitions (the common case keeps
+  // them for the weights); later chunks are re-read
+  const float ls0 = lane < a.parts ? a.part_lse[(int64_t)lane * a.rows + row] : -INFINITY;
+  float M = ls0;
+  bool nan = !(ls0 == ls0);
+  for (int s = lane + 64; s < a.parts; s += 64) {
+    const float x = a.part_lse[(int64_t)s * a.rows + row];
+    nan |= !(x == x);
+    M = fmaxf(M, x);
   }
   M = wave_max(M);
   nan = __any(nan);
@@ -41,21 +67,21 @@ __global__ void __launch_bounds__(256) lse_merge_kernel(MergeLaunch a) {
   float den = 0.0f;
   if (!nan && M != -INFINITY) {
     for (int base = 0; base < a.parts; base += 64) {
-      const int s_l = base + lane;
-      const float ls = s_l < a.parts ? a.part_lse[(int64_t)s_l * a.rows + row] : -INFINITY;
+      const float ls = base == 0 ? ls0
+                                 : (base + lane < a.parts ? a.part_lse[(int64_t)(base + lane) * a.rows + row]
+                                                          : -INFINITY);
       const float w_l = ls == -INFINITY ? 0.0f : expf(ls - M);
       const int n = min(64, a.parts - base);
-      for (int k = 0; k < n; ++k) {
-        const float w = __shfl(w_l, k);
-        if (w == 0.0f) continue;             // empty partition: its out is not read
-        den += w;
-        const float* o = a.part_out + ((int64_t)(base + k) * a.rows + row) * D + lane * PER;
-        if constexpr (PER == 2) {
-          const float2 v = *reinterpret_cast<const float2*>(o);
-          acc[0] = fmaf(w, v.x, acc[0]);
-          acc[1] = fmaf(w, v.y, acc[1]);
-        } else {
-          acc[0] = fmaf(w, o[0], acc[0]);
+      for (int k0 = 0; k0 < n; k0 += BATCH) {
+        if (base != 0 || k0 != 0) load_batch(v, base + k0, n - k0);
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+          const float w = k0 + j < n ? __shfl(w_l, k0 + j) : 0.0f;
+          if (w != 0.0f) {
+            den += w;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, v[j][i], acc[i]);
+          }
         }
       }
     }

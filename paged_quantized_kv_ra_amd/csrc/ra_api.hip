@@ -204,6 +204,9 @@ int32_t ra_kv_store(const void* k, const void* v, int32_t src_dtype, int64_t k_t
   if (k_token_stride < (int64_t)num_kv_heads * head_dim || v_token_stride < (int64_t)num_kv_heads * head_dim)
     return fail(RA_ERR_INVALID_ARG, "ra_kv_store: token strides (%lld, %lld) smaller than num_kv_heads * head_dim",
                 (long long)k_token_stride, (long long)v_token_stride);
+  if (num_tokens > (int64_t)(1 << 30) / ((int64_t)num_kv_heads * (head_dim / 8)))
+    return fail(RA_ERR_INVALID_ARG,
+                "ra_kv_store: num_tokens * num_kv_heads * head_dim / 8 must not exceed 2^30; store in chunks");
   if (num_tokens == 0) return RA_OK;
   if (!k || !v || !slot_mapping || !k_cache || !v_cache)
     return fail(RA_ERR_INVALID_ARG, "ra_kv_store: k, v, slot_mapping, k_cache and v_cache must be non-NULL");

@@ -207,6 +207,7 @@ def _store(lib, **kw):
     (dict(k=0), 1, "non-NULL"),
     (dict(kc=FAKE + 1), 3, "aligned"),
     (dict(ks=260), 3, "multiples of 8"),
+    (dict(n=(1 << 30) // 32 + 1), 1, "store in chunks"),
 ])
 def test_store_validation(kw, status, msg):
     L = _lib()
