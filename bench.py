@@ -27,7 +27,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_HBM_GBS = 8000.0
 POOL_ROTATION_BYTES = 1 << 30
-KERNEL_SOURCES = ["paged_quantized_kv_ra_amd/csrc/attn_mfma.hip", "paged_quantized_kv_ra_amd/csrc/attn_vec.hip",
+KERNEL_SOURCES = ["paged_quantized_kv_ra_amd/csrc/attn_mfma.hip",
                   "paged_quantized_kv_ra_amd/csrc/attn_common.h", "paged_quantized_kv_ra_amd/csrc/ra_device.h",
                   "paged_quantized_kv_ra_amd/csrc/ra_internal.h"]
 
@@ -346,8 +346,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": traffic, "kernel": "attn_mfma_kernel" if w.num_q_heads // w.num_kv_heads
-                     * w.max_q_len >= 16 else "attn_vec_kernel",
+                     "traffic": traffic, "kernel": "attn_mfma_kernel",
                      "algorithmic_bytes_per_launch": alg, "attn_us": round(attn_avg_ms * 1e3, 2),
                      "kernel_source_hash": src_hash},
         "attended_tokens_per_step": tokens,

@@ -23,13 +23,17 @@ struct UnitPages {
   __device__ __forceinline__ int32_t page(int32_t n) const { return n < na ? p0a + n : p0b + (n - na); }
 };
 
-// Partition size (tokens, a multiple of 16) of sequence b.
-__device__ __forceinline__ int32_t partition_tokens(const AttnLaunch& a, int32_t ctx) {
+// Partition size (tokens, a multiple of 16) of a sequence with the given
+// context and row count.
+__device__ __forceinline__ int32_t partition_tokens(const AttnLaunch& a, int32_t ctx, int32_t rows) {
   if (a.num_splits > 0) {
     const int32_t per = (ctx + a.num_splits - 1) / a.num_splits;
     return ((per + kPage - 1) / kPage) * kPage;
   }
-  return a.part_tokens;
+  if (rows >= kSmallUnitRows) return a.part_tokens;
+  const int32_t per = (ctx + kSmallSplits - 1) / kSmallSplits;
+  const int32_t p = ((per + kPage - 1) / kPage) * kPage;
+  return min(max(p, a.part_small), a.part_tokens);
 }
 
 // Visible page ranges of partition [lo, hi) for a block of q_len queries.

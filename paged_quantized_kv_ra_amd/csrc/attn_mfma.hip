@@ -1,25 +1,28 @@
-// attn_mfma.hip -- grouped verify attention on the gfx950 matrix cores.
+// attn_mfma.hip -- decode and verify attention on the gfx950 matrix cores.
 //
-// Used when a (sequence, KV head) unit has g * q_len >= 16 query rows (the
-// pages' MTP4 verify block of 1 + 4 tokens times the query heads of one KV
-// head: ReVolta README, intro list and "Quick start").  The KV cache is read
-// once, straight into registers, and converted exactly to FP16 operands (the
-// pages' V100 converts stored KV to FP16 for the arithmetic: ReVolta README,
-// "Weight and KV formats").
+// One (sequence, KV head) unit has g * q_len query rows: the pages' MTP4
+// verify block of 1 + 4 tokens times the query heads of one KV head (ReVolta
+// README, intro list and "Quick start"), or g rows for plain decode.  Rows are
+// processed in 16-row tiles; a decode unit with fewer rows uses one padded
+// tile (the path is bound by HBM, not by the matrix cores).  The KV cache is
+// converted exactly to FP16 operands in registers (the pages' V100 converts
+// stored KV to FP16 for the arithmetic: ReVolta README, "Weight and KV
+// formats").
 //
 // Per wavefront and 16-token page, for each 16-row tile of query rows:
 //   S^T[16 keys][16 rows] = K[16][D] . Q^T[D][16]      v_mfma_f32_16x16x32_f16 (D/32 steps)
 //   P^T = exp2(c * S^T - c * m)                       online softmax, fp32, rescaled lazily
 //   O^T[D][16 rows]      += V^T[D][16] . P^T[16][16]   v_mfma_f32_16x16x16_f16 (D/16 tiles)
-// The cache layout puts every lane's 16-byte loads directly in the operand
-// order of both products: a K lane holds one token's contiguous D/4 dims, a V
-// lane holds four consecutive tokens of D/16 dims, and the S^T accumulator
-// layout (lane = row + 16 * token-quad) is exactly the P^T operand layout, so
-// no data moves between lanes or through LDS in the hot loop.  Pages stream
-// through a ring of NBUF register buffers, NBUF - 1 pages in flight per wave.
+// The cache layout puts every lane's 16-byte piece of a page directly in the
+// operand order of both products: a K lane holds one token's contiguous D/4
+// dims, a V lane holds four consecutive tokens of D/16 dims, and the S^T
+// accumulator layout (lane = row + 16 * token-quad) is exactly the P^T operand
+// layout, so no data moves between lanes in the hot loop.  Pages stream into a
+// per-wave LDS ring by DMA (global_load_lds), NRING - 1 pages in flight per
+// wave, and each lane reads back its own 16-byte pieces.
 //
-// A workgroup has 8 waves (two per SIMD) that take pages round-robin; their partial
-// (m, l, O) are combined through LDS in a fixed order at the end.
+// A workgroup has 8 waves (two per SIMD) that take pages round-robin; their
+// partial (m, l, O) are combined through LDS in a fixed order at the end.
 #include "attn_common.h"
 
 namespace ra {
@@ -287,7 +290,7 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a,
   const int32_t g = a.hq / a.hkv;
   const int32_t q_len = q1 - q0;
   const int32_t rows = g * q_len;
-  if (rows < kMfmaMinRows) return;                      // the vector kernel's unit
+  if (rows == 0) return;
   const int32_t row0 = u.rg * kMfmaRowsPerBlock;
   if (row0 >= rows) return;
   const int32_t ctx = a.context_lens[u.b];
@@ -297,7 +300,7 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a,
   int32_t lo = 0, hi = 0;
   UnitPages pg{0, 0, 0, 0};
   if (!bad) {
-    const int32_t P = partition_tokens(a, ctx);
+    const int32_t P = partition_tokens(a, ctx, rows);
     lo = u.s * P;
     hi = min(lo + P, ctx);
     pg = unit_pages(a, ctx, q_len, lo, hi);

@@ -51,9 +51,8 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Split plan of an attention call: partition slots per sequence and, in the
 // automatic mode, each kernel's fixed partition size.
 struct Plan {
-  bool use_mfma, use_vec;
   int32_t slots;
-  int32_t part_mfma, part_vec;
+  int32_t part_large, part_small;
   bool direct;
 };
 
@@ -99,16 +98,24 @@ int32_t check_attn(const ra_attn_args* a, Plan* plan) {
   const int64_t g = a->num_q_heads / a->num_kv_heads;
   const int64_t rows_max = g * a->max_q_len;
   const int64_t rows_min = g * (a->min_q_len > 0 ? a->min_q_len : 1);
-  plan->use_mfma = rows_max >= ra::kMfmaMinRows;
-  plan->use_vec = rows_min < ra::kMfmaMinRows;
-  plan->part_mfma = ra::kAutoPartMfma;
-  plan->part_vec = ra::kAutoPartVec;
+  plan->part_large = ra::kAutoPartLarge;
+  plan->part_small = ra::kAutoPartSmall;
   if (a->num_splits > 0) {
     plan->slots = a->num_splits;
   } else {
+    // the partition size is chosen per sequence by its row count; the grid
+    // holds enough slots for either kind the bounds admit
     int64_t s = 1;
-    if (plan->use_mfma) s = std::max<int64_t>(s, ceil_div(a->max_context_len, plan->part_mfma));
-    if (plan->use_vec) s = std::max<int64_t>(s, ceil_div(a->max_context_len, plan->part_vec));
+    if (rows_max >= ra::kSmallUnitRows) s = std::max<int64_t>(s, ceil_div(a->max_context_len, plan->part_large));
+    if (rows_min < ra::kSmallUnitRows) {
+      // decode units: at most kSmallSplits partitions up to kSmallSplits * kAutoPartLarge
+      // tokens, kAutoPartLarge-token partitions beyond
+      const int64_t c = a->max_context_len;
+      const int64_t sm = c <= (int64_t)ra::kSmallSplits * plan->part_large
+                             ? std::min<int64_t>(ra::kSmallSplits, ceil_div(c, plan->part_small))
+                             : ceil_div(c, plan->part_large);
+      s = std::max<int64_t>(s, sm);
+    }
     if (s > RA_KV_MAX_SPLITS * 64)
       return fail(RA_ERR_INVALID_ARG, "ra_paged_attn: max_context_len %d needs too many partitions",
                   a->max_context_len);
@@ -117,9 +124,7 @@ int32_t check_attn(const ra_attn_args* a, Plan* plan) {
   plan->direct = plan->slots == 1 && a->out != nullptr;
 
   // grid size: slots * Hkv * row groups * batch blocks
-  const int64_t rg = std::max<int64_t>(ceil_div(rows_max, ra::kMfmaRowsPerBlock),
-                                       ceil_div(std::min<int64_t>(rows_max, ra::kMfmaMinRows - 1),
-                                                ra::kVecRowsPerBlock));
+  const int64_t rg = ceil_div(rows_max, ra::kMfmaRowsPerBlock);
   if ((int64_t)plan->slots * a->num_kv_heads * rg * a->batch > (int64_t)0x7FFFFFF0)
     return fail(RA_ERR_INVALID_ARG, "ra_paged_attn: problem needs more than 2^31 workgroups");
   return RA_OK;
@@ -244,16 +249,10 @@ int32_t ra_paged_attn(const ra_attn_args* args, void* stream) {
   const hipStream_t s = static_cast<hipStream_t>(stream);
   ra::AttnLaunch L = make_launch(args, p);
   hipError_t e = hipSuccess;
-  if (p.use_mfma) {
-    L.part_tokens = p.part_mfma;
-    e = ra::launch_attn_mfma(L, s);
-    if (e != hipSuccess) return fail(RA_ERR_HIP, "ra_paged_attn: matrix-core kernel launch failed: %s", hipGetErrorString(e));
-  }
-  if (p.use_vec) {
-    L.part_tokens = p.part_vec;
-    e = ra::launch_attn_vec(L, s);
-    if (e != hipSuccess) return fail(RA_ERR_HIP, "ra_paged_attn: vector kernel launch failed: %s", hipGetErrorString(e));
-  }
+  L.part_tokens = p.part_large;
+  L.part_small = p.part_small;
+  e = ra::launch_attn_mfma(L, s);
+  if (e != hipSuccess) return fail(RA_ERR_HIP, "ra_paged_attn: attention kernel launch failed: %s", hipGetErrorString(e));
   if (!p.direct && args->out) {
     ra::MergeLaunch M{args->partial_out, args->partial_lse, p.slots, (int64_t)args->total_q * args->num_q_heads,
                       args->head_dim, args->out, args->q_dtype, args->lse};

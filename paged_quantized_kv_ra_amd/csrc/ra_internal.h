@@ -73,23 +73,28 @@ struct AttnLaunch {
   int32_t sinks;
   int32_t num_splits;    // > 0 explicit, 0 auto
   int32_t slots;         // partition slots per sequence in the grid
-  int32_t part_tokens;   // auto mode: fixed partition size in tokens
+  int32_t part_tokens;   // auto mode: partition size (tokens) of units with >= kSmallUnitRows rows
+  int32_t part_small;    // auto mode: partition size of units with fewer rows
   bool direct;           // write out/lse directly (one slot)
 };
 
-// Rows of a (sequence, KV head) unit: g * q_len.  Sequences with
-// g * q_len >= kMfmaMinRows use the matrix-core kernel, the rest the
-// vector kernel.
-constexpr int kMfmaMinRows = 16;
+// Rows of a (sequence, KV head) unit: g * q_len, in 16-row matrix-core tiles
+// (a decode unit with fewer rows uses one padded tile), at most
+// kMfmaRowsPerBlock rows per workgroup.
 constexpr int kMfmaRowsPerBlock = 48;   // rows beyond this split over row groups
-constexpr int kVecRowsPerBlock = 8;
 
-// Automatic partition sizes (tokens), constants of the library.
-constexpr int kAutoPartMfma = 2048;
-constexpr int kAutoPartVec = 256;
+// Automatic partitions (num_splits = 0).  Units with at least kSmallUnitRows
+// rows use kAutoPartLarge tokens.  Smaller (decode) units take about
+// kSmallSplits partitions of their own sequence's context, clamped to
+// [kAutoPartSmall, kAutoPartLarge] tokens, so that a decode batch still fills
+// the chip while long contexts keep few partials.  Either rule depends only on
+// the sequence itself, never on the rest of the batch.
+constexpr int kSmallUnitRows = 16;
+constexpr int kAutoPartLarge = 2048;
+constexpr int kAutoPartSmall = 512;
+constexpr int kSmallSplits = 32;
 
 hipError_t launch_attn_mfma(const AttnLaunch& a, hipStream_t s);
-hipError_t launch_attn_vec(const AttnLaunch& a, hipStream_t s);
 
 struct MergeLaunch {
   const float* part_out;

@@ -266,6 +266,14 @@ def verify_fp8_32k():
                  pool_pages=16384)
 
 
+def decode_fp8_32k():
+    """Plain decode (q_len 1) over the 8 x 32K E4M3 shape: an extra measurement
+    of the decode rows (g = 8 < 16) on long contexts."""
+    return build("decode_e4m3_8x32k_q1", 5, ctx=[32 * K] * 8, q_len=1, num_q_heads=16,
+                 num_kv_heads=2, head_dim=128, kv_dtype="e4m3", q_dtype="f16",
+                 pool_pages=16384)
+
+
 def prefix_int8_256k():
     """4 x 256K sharing the first 192K tokens' pages, INT8 KV, q_len 5."""
     return build("prefix_int8_4x256k_shared192k_q5", 3, ctx=[256 * K] * 4, q_len=5,
@@ -293,6 +301,7 @@ BENCH_WORKLOADS = {
     "tiny_decode": tiny_decode,
     "batch8_decode": batch8_decode,
     "verify_fp8_32k": verify_fp8_32k,
+    "decode_fp8_32k": decode_fp8_32k,
     "prefix_int8_256k": prefix_int8_256k,
     "split_fp8_512k": split_fp8_512k,
     "split_fp8_512k_sliding": split_fp8_512k_sliding,

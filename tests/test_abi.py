@@ -172,9 +172,11 @@ def test_fp16_cache_ignores_scales_and_workspace_query():
     assert slots == 3 and po == 3 * 10 * 16 * 128 and pl == 3 * 10 * 16
     a = _good_args(L, num_splits=64, block_table_stride=1000, max_context_len=16000)
     assert L.paged_attn_workspace(a)[0] == 64
-    # decode rows (g * q_len < 16) use the vector kernel's 256-token partitions
-    a = _good_args(L, num_splits=0, max_q_len=1, min_q_len=1, block_table_stride=1000, max_context_len=5000)
-    assert L.paged_attn_workspace(a)[0] == 20
+    # decode units (g * q_len < 16 rows): 512-token partitions up to 16K tokens,
+    # at most 32 up to 64K, 2048-token partitions beyond
+    for ctx, slots in [(5000, 10), (16384, 32), (40000, 32), (65536, 32), (100000, 49)]:
+        a = _good_args(L, num_splits=0, max_q_len=1, min_q_len=1, block_table_stride=7000, max_context_len=ctx)
+        assert L.paged_attn_workspace(a)[0] == slots, ctx
 
 
 def test_empty_batch_is_ok_without_pointers():

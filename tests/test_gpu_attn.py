@@ -14,13 +14,13 @@ pytestmark = pytest.mark.gpu
 
 # name, ctx, q_len, Hq, Hkv, D, kv, q dtype, window, sinks, num_splits
 CASES = [
-    ("vec_g4_d64_f16", [37, 300, 16, 1, 257], 1, 4, 1, 64, "f16", "f16", -1, 0, 1),
-    ("vec_g8_f16_bf16q_auto", [1000, 77, 513, 2100], 1, 16, 2, 128, "f16", "bf16", -1, 0, 0),
-    ("vec_g8_e4m3", [1000, 77, 513], 1, 16, 2, 128, "e4m3", "f16", -1, 0, 1),
-    ("vec_g8_int8_split3", [1000, 77, 513], 1, 16, 2, 128, "int8", "f16", -1, 0, 3),
-    ("vec_g1_q2_d64_e4m3", [200, 31, 2], 2, 2, 2, 64, "e4m3", "f16", -1, 0, 1),
-    ("vec_g4_q3_int8_rowgroups", [150, 64], 3, 8, 2, 128, "int8", "bf16", -1, 0, 2),
-    ("vec_g8_window_sinks", [900, 120], 1, 16, 2, 128, "e4m3", "f16", 100, 4, 0),
+    ("dec_g4_d64_f16", [37, 300, 16, 1, 257], 1, 4, 1, 64, "f16", "f16", -1, 0, 1),
+    ("dec_g8_f16_bf16q_auto", [1000, 77, 513, 2100], 1, 16, 2, 128, "f16", "bf16", -1, 0, 0),
+    ("dec_g8_e4m3", [1000, 77, 513], 1, 16, 2, 128, "e4m3", "f16", -1, 0, 1),
+    ("dec_g8_int8_split3", [1000, 77, 513], 1, 16, 2, 128, "int8", "f16", -1, 0, 3),
+    ("dec_g1_q2_d64_e4m3", [200, 31, 2], 2, 2, 2, 64, "e4m3", "f16", -1, 0, 1),
+    ("dec_g4_q3_int8_rowgroups", [150, 64], 3, 8, 2, 128, "int8", "bf16", -1, 0, 2),
+    ("dec_g8_window_sinks", [900, 120], 1, 16, 2, 128, "e4m3", "f16", 100, 4, 0),
     ("mfma_g8_q5_e4m3", [1000, 77, 513, 5, 4097], 5, 16, 2, 128, "e4m3", "f16", -1, 0, 1),
     ("mfma_g8_q5_e4m3_auto", [1000, 77, 513, 5, 4097], 5, 16, 2, 128, "e4m3", "f16", -1, 0, 0),
     ("mfma_g8_q5_int8_split7", [1000, 77, 513, 40], 5, 16, 2, 128, "int8", "f16", -1, 0, 7),
@@ -36,7 +36,10 @@ CASES = [
     ("mfma_g8_q16_window37_direct", [1000, 333, 70], 16, 16, 2, 128, "e4m3", "f16", 37, 0, 1),
     ("mfma_g8_q7_window100_sink20", [1000, 517], 7, 16, 2, 128, "int8", "f16", 100, 20, 1),
     ("mfma_g8_q5_window250_auto", [3000, 260], 5, 16, 2, 128, "f16", "f16", 250, 4, 0),
-    ("vec_g4_q3_window45", [700, 90], 3, 8, 2, 128, "e4m3", "f16", 45, 2, 1),
+    ("dec_g4_q3_window45", [700, 90], 3, 8, 2, 128, "e4m3", "f16", 45, 2, 1),
+    # decode auto partitions around their rule's bends: 512 tokens up to 16K,
+    # ~32 partitions up to 64K, 2048 tokens beyond
+    ("dec_g8_e4m3_auto_bends", [16384, 16400, 65536, 65552, 100000, 511], 1, 16, 2, 128, "e4m3", "f16", -1, 0, 0),
 ]
 
 
@@ -133,10 +136,11 @@ def _single(w, b):
     return q0, q1
 
 
-@pytest.mark.parametrize("case", [CASES[1], CASES[8], CASES[14], CASES[17]], ids=lambda c: c[0])
+@pytest.mark.parametrize("case", [CASES[1], CASES[8], CASES[14], CASES[17], CASES[22]], ids=lambda c: c[0])
 def test_batch_invariance_bitwise(case):
     """A sequence's result does not depend on the rest of the batch (other
-    lengths change the automatic split count and the kernels launched)."""
+    lengths change the automatic split count, and mixing decode with verify
+    blocks changes the row tiles of the launch)."""
     w = _build(case)
     dw = DeviceWorkload(w)
     out, lse = dw.attn()

@@ -16,7 +16,7 @@ from gpu_util import DeviceWorkload, log, t_src
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    ("vec_g8_e4m3_split3", [1000, 77, 513], 1, 16, 2, 128, "e4m3", "f16", -1, 0, 3),
+    ("dec_g8_e4m3_split3", [1000, 77, 513], 1, 16, 2, 128, "e4m3", "f16", -1, 0, 3),
     ("mfma_g8_q5_int8_auto_bf16", [1000, 77, 5000], 5, 16, 2, 128, "int8", "bf16", -1, 0, 0),
     ("mixed_window_sinks", [500, 400, 300], [1, 5, 16], 16, 2, 128, "e4m3", "f16", 100, 4, 2),
 ]
