@@ -107,60 +107,3 @@ __device__ __forceinline__ bool seq_ok(const AttnLaunch& a, int32_t ctx, int32_t
 }
 
 }  // namespace ra
-
-namespace ra {
-
-// Physical page ids of the pages one wavefront visits, prefetched into a VGPR
-// 64 at a time: lane j of chunk c holds the raw block-table entry of the
-// wave's (64c + j)-th page; it is read back with readlane when that page's
-// loads are issued and checked there (an id outside [0, num_pages) makes the
-// unit `bad` and is replaced by page 0, so every load stays in bounds).  The
-// following chunk is requested while the current one is consumed.
-struct PageIdChunks {
-  int32_t cur, next;   // per-lane ids of the current and the following chunk
-  int32_t chunk;       // index of the chunk held in `cur`
-};
-
-// Logical page index (within the unit) of the wave's k-th page: steps of
-// PAGES_PER_STEP consecutive pages are dealt to the WAVES waves round-robin.
-template <int PAGES_PER_STEP, int WAVES>
-__device__ __forceinline__ int32_t wave_page(int32_t wave, int32_t k) {
-  return PAGES_PER_STEP * (wave + WAVES * (k / PAGES_PER_STEP)) + k % PAGES_PER_STEP;
-}
-
-template <int PAGES_PER_STEP, int WAVES>
-__device__ __forceinline__ int32_t load_id_chunk(const UnitPages& pg, int32_t npages, const int32_t* bt_row,
-                                                 int32_t wave, int32_t chunk, int lane) {
-  const int32_t n = wave_page<PAGES_PER_STEP, WAVES>(wave, chunk * 64 + lane);
-  return n < npages ? bt_row[pg.page(n)] : 0;
-}
-
-template <int PAGES_PER_STEP, int WAVES>
-__device__ __forceinline__ void init_ids(PageIdChunks& c, const UnitPages& pg, int32_t npages,
-                                         const int32_t* bt_row, int32_t wave, int lane) {
-  c.cur = load_id_chunk<PAGES_PER_STEP, WAVES>(pg, npages, bt_row, wave, 0, lane);
-  c.next = load_id_chunk<PAGES_PER_STEP, WAVES>(pg, npages, bt_row, wave, 1, lane);
-  c.chunk = 0;
-}
-
-// Checked physical id of the wave's k-th page (k non-decreasing between
-// calls); `live` says whether that page belongs to the unit.
-template <int PAGES_PER_STEP, int WAVES>
-__device__ __forceinline__ int32_t page_id(PageIdChunks& c, const AttnLaunch& a, const UnitPages& pg,
-                                           int32_t npages, const int32_t* bt_row, int32_t wave, int32_t k,
-                                           int lane, bool live, bool& bad) {
-  const int32_t ch = k >> 6;
-  if (ch != c.chunk) {       // wave-uniform, once per 64 pages
-    c.cur = c.next;
-    c.chunk = ch;
-    c.next = load_id_chunk<PAGES_PER_STEP, WAVES>(pg, npages, bt_row, wave, ch + 1, lane);
-  }
-  int32_t id = __builtin_amdgcn_readlane(c.cur, k & 63);
-  if (id < 0 || id >= a.num_pages) {
-    bad = bad || live;
-    id = 0;
-  }
-  return live ? id : 0;
-}
-
-}  // namespace ra

@@ -21,8 +21,9 @@
 // per-wave LDS ring by DMA (global_load_lds), NRING - 1 pages in flight per
 // wave, and each lane reads back its own 16-byte pieces.
 //
-// A workgroup has 8 waves (two per SIMD) that take pages round-robin; their
-// partial (m, l, O) are combined through LDS in a fixed order at the end.
+// A workgroup has 8 waves (two per SIMD) that take contiguous shares of the
+// unit's pages; their partial (m, l, O) are combined through LDS in a fixed
+// order at the end.
 #include "attn_common.h"
 
 namespace ra {
@@ -62,17 +63,24 @@ struct PageRegs {
 // Page ids of the pages one wave visits, staged 64 at a time in LDS by the
 // same DMA path as the pages, so that the wave's vector-memory counter only
 // tracks loads whose order the ring accounts for.  Lane j of chunk c holds the
-// raw block-table entry of the wave's (64 c + j)-th page (logical page
-// wave + 8 (64 c + j)); chunk c + 1 is requested when chunk c is taken up.
+// raw block-table entry of the wave's (64 c + j)-th page; chunk c + 1 is
+// requested when chunk c is taken up.
 struct IdRing {
   int32_t cur;     // per-lane ids of chunk `chunk`
   int32_t chunk;
 };
 
-__device__ __forceinline__ void id_dma(int32_t* slot, const UnitPages& pg, int32_t npages, const int32_t* bt_row,
-                                       int32_t wave, int32_t chunk, int lane) {
-  const int32_t n = wave + kWaves * (chunk * 64 + lane);
-  if (n < npages) __builtin_amdgcn_global_load_lds(bt_row + pg.page(n), (lds_u8*)slot, 4, 0, 0);
+// The unit's pages a wave visits: its k-th page (k < count) is the unit's
+// logical page first + stride * k.
+struct WaveSpan {
+  int32_t first, stride, count;
+  __device__ __forceinline__ int32_t page(int32_t k) const { return first + stride * k; }
+};
+
+__device__ __forceinline__ void id_dma(int32_t* slot, const UnitPages& pg, const WaveSpan& ws, const int32_t* bt_row,
+                                       int32_t chunk, int lane) {
+  const int32_t k = chunk * 64 + lane;
+  if (k < ws.count) __builtin_amdgcn_global_load_lds(bt_row + pg.page(ws.page(k)), (lds_u8*)slot, 4, 0, 0);
 }
 
 // Checked physical id of the wave's k-th page (k non-decreasing).  On entry to
@@ -80,13 +88,13 @@ __device__ __forceinline__ void id_dma(int32_t* slot, const UnitPages& pg, int32
 // than the last NRING - 1 pages, and a chunk is requested 64 pages before use.
 // An id outside [0, num_pages) makes the unit bad and reads page 0 instead.
 __device__ __forceinline__ int32_t ring_page_id(IdRing& r, int32_t (*sm_id)[64], const AttnLaunch& a,
-                                                const UnitPages& pg, int32_t npages, const int32_t* bt_row,
-                                                int32_t wave, int32_t k, int lane, bool& bad) {
+                                                const UnitPages& pg, const WaveSpan& ws, const int32_t* bt_row,
+                                                int32_t k, int lane, bool& bad) {
   const int32_t ch = k >> 6;
   if (ch != r.chunk) {       // wave-uniform, once per 64 pages
     r.chunk = ch;
     r.cur = sm_id[ch & 1][lane];
-    id_dma(sm_id[(ch + 1) & 1], pg, npages, bt_row, wave, ch + 1, lane);
+    id_dma(sm_id[(ch + 1) & 1], pg, ws, bt_row, ch + 1, lane);
   }
   int32_t id = __builtin_amdgcn_readlane(r.cur, k & 63);
   if (id < 0 || id >= a.num_pages) {
@@ -102,10 +110,10 @@ __device__ __forceinline__ int32_t ring_page_id(IdRing& r, int32_t (*sm_id)[64],
 // cache layout has in HBM.
 template <int KV, int D>
 __device__ __forceinline__ void issue_page(uint8_t (*ring)[kSlab], IdRing& ids, int32_t (*sm_id)[64],
-                                           const AttnLaunch& a, const UnitPages& pg, int32_t npages, int32_t wave,
+                                           const AttnLaunch& a, const UnitPages& pg, const WaveSpan& ws,
                                            int32_t i, const int32_t* bt_row, int h, int lane, bool& bad) {
   using G = Geo<KV, D>;
-  const int32_t pid = ring_page_id(ids, sm_id, a, pg, npages, bt_row, wave, i, lane, bad);
+  const int32_t pid = ring_page_id(ids, sm_id, a, pg, ws, bt_row, i, lane, bad);
   const int64_t blk = ((int64_t)pid * a.hkv + h) * G::BLK;
   const uint8_t* kp = a.k_cache + blk + (uint32_t)lane * 16u;
   const uint8_t* vp = a.v_cache + blk + (uint32_t)lane * 16u;
@@ -310,8 +318,17 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a,
 
   // first two chunks of the wave's page ids (DMA into LDS)
   int32_t (*sm_id)[64] = sm_ids[wave];
-  id_dma(sm_id[0], pg, npages, bt_row, wave, 0, lane);
-  id_dma(sm_id[1], pg, npages, bt_row, wave, 1, lane);
+  // Each wave takes a contiguous share of the unit's pages.  On each SIMD the
+  // older wave (0-3) wins issue arbitration over its partner (4-7) and runs
+  // about a fifth faster, so it takes 9 of every 16 pages of the pair: both
+  // then finish together.  The split depends only on the page count.
+  constexpr int32_t kFast = 9, kSlow = 16 - kFast;
+  const int32_t cum0 = wave < 4 ? wave * kFast : 4 * kFast + (wave - 4) * kSlow;
+  const int32_t cum1 = cum0 + (wave < 4 ? kFast : kSlow);
+  const int32_t p0 = (int32_t)(((int64_t)npages * cum0) >> 6), p1 = (int32_t)(((int64_t)npages * cum1) >> 6);
+  const WaveSpan ws{p0, 1, p1 - p0};
+  id_dma(sm_id[0], pg, ws, bt_row, 0, lane);
+  id_dma(sm_id[1], pg, ws, bt_row, 1, lane);
   const uint32_t lane_off = (uint32_t)lane * 16u;
 
   // query fragments: lane (kgrp, ncol) holds row ncol of each 16-row tile,
@@ -360,11 +377,11 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a,
   const float c = a.softmax_scale * a.k_scale * kLog2e;
   const float thr = kLazy / c;
 
-  // ---- main loop over the wave's pages (page wave + 8 k) through the LDS
+  // ---- main loop over the wave's pages through the LDS
   // ring: page k computes from slot k % NRING while pages k + 1 .. k + NRING - 1
   // are in flight; once its slab reads have retired, page k + NRING is issued
   // into the slot it freed.
-  const int32_t my_pages = npages > wave ? (npages - wave + kWaves - 1) / kWaves : 0;
+  const int32_t my_pages = ws.count;
   if (my_pages > 0) {
     constexpr int NR = G::NRING;
     uint8_t (*ring)[kSlab] = &sm_raw[wave * NR * G::NSL];
@@ -372,7 +389,7 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a,
 #pragma unroll
     for (int j = 0; j < NR; ++j)
       if (j < my_pages)
-        issue_page<KV, D>(ring + j * G::NSL, ids, sm_id, a, pg, npages, wave, j, bt_row, u.h, lane, bad);
+        issue_page<KV, D>(ring + j * G::NSL, ids, sm_id, a, pg, ws, j, bt_row, u.h, lane, bad);
     for (int32_t i = 0; i < my_pages; i += NR) {
 #pragma unroll
       for (int j = 0; j < NR; ++j) {
@@ -386,12 +403,12 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a,
             wait_vmcnt<0>();
           PageRegs<KV, D> r;
           read_page<KV, D>(r, ring + j * G::NSL, lane_off);
-          compute_page<KV, D, NT>(acc, r, qf, a, pg, wave + kWaves * k, ctx, q_len, pos, kgrp, c, thr);
+          compute_page<KV, D, NT>(acc, r, qf, a, pg, ws.page(k), ctx, q_len, pos, kgrp, c, thr);
           // the slot's reads have returned (their values were consumed) before
           // the next load may overwrite it
           wait_lgkmcnt0();
           if (k + NR < my_pages)
-            issue_page<KV, D>(ring + j * G::NSL, ids, sm_id, a, pg, npages, wave, k + NR, bt_row, u.h, lane, bad);
+            issue_page<KV, D>(ring + j * G::NSL, ids, sm_id, a, pg, ws, k + NR, bt_row, u.h, lane, bad);
         }
       }
     }
