@@ -282,7 +282,7 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a,
   constexpr int kMergeBytes = kPairs * kWaves * kWave * G::MT * 4;
   constexpr int kRawBytes = kRingBytes > kMergeBytes ? kRingBytes : kMergeBytes;
   __shared__ __attribute__((aligned(16))) uint8_t sm_raw[kRawBytes / kSlab][kSlab];
-  __shared__ float sm_ml[2][kWaves][NT * 16];
+  __shared__ f32x4 sm_ml[2][NT * 16][kWaves / 4];   // per row: the 8 waves' m (l), read as 2 x 16 B
   __shared__ int32_t sm_ids[kWaves][2][64];
   __shared__ int32_t sm_bad[kWaves];
 
@@ -423,8 +423,8 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a,
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
     if (kgrp == 0) {
-      sm_ml[0][wave][nt * 16 + ncol] = acc.m[nt];
-      sm_ml[1][wave][nt * 16 + ncol] = l;
+      reinterpret_cast<float*>(&sm_ml[0][nt * 16 + ncol][0])[wave] = acc.m[nt];
+      reinterpret_cast<float*>(&sm_ml[1][nt * 16 + ncol][0])[wave] = l;
     }
   }
   if (lane == 0) sm_bad[wave] = bad ? 1 : 0;
@@ -435,16 +435,25 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a,
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int rr = nt * 16 + ncol;
+    float mw[kWaves], lw[kWaves];
+#pragma unroll
+    for (int q = 0; q < kWaves / 4; ++q) {
+      const f32x4 m4 = sm_ml[0][rr][q], l4 = sm_ml[1][rr][q];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        mw[4 * q + j] = m4[j];
+        lw[4 * q + j] = l4[j];
+      }
+    }
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_ml[0][w][rr]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mw[w]);
     float L = 0.0f;
     fself[nt] = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float mw = sm_ml[0][w][rr];
-      const float f = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((mw - M) * c);
-      L += f * sm_ml[1][w][rr];
+      const float f = (mw[w] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((mw[w] - M) * c);
+      L += f * lw[w];
       if (w == wave) fself[nt] = f;
     }
     Mrow[nt] = M;
@@ -457,17 +466,17 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a,
   // row nt * 16 + ncol; every wave stores them, then wave w < 2 NT sums pair
   // w = (nt, i) over the waves in wave order and writes that slice of the
   // output (same lanes, so the row and its (M, L) are the lane's own).
-  float* red = reinterpret_cast<float*>(&sm_raw[0][0]);   // [kPairs][kWaves][kWave][MT]
+  f32x4* red = reinterpret_cast<f32x4*>(&sm_raw[0][0]);   // [kPairs][kWaves][MT / 4][kWave]
   const float vs = a.v_scale;
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
 #pragma unroll
     for (int pr = 0; pr < kPairs; ++pr) {
       const int nt = pr >> 1, i = 2 * p + (pr & 1);
-      float* dst = red + ((pr * kWaves + wave) * kWave + lane) * G::MT;
+      f32x4* dst = red + (pr * kWaves + wave) * (G::MT / 4) * kWave + lane;
 #pragma unroll
       for (int k = 0; k < G::MT / 4; ++k)
-        *reinterpret_cast<f32x4*>(dst + 4 * k) =
+        dst[k * kWave] =
             f32x4{acc.o[4 * k][nt][i], acc.o[4 * k + 1][nt][i], acc.o[4 * k + 2][nt][i], acc.o[4 * k + 3][nt][i]} *
             fself[nt];
     }
@@ -480,10 +489,10 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a,
       for (int mt = 0; mt < G::MT; ++mt) v[mt] = 0.0f;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const float* src = red + ((pr * kWaves + w) * kWave + lane) * G::MT;
+        const f32x4* src = red + (pr * kWaves + w) * (G::MT / 4) * kWave + lane;
 #pragma unroll
         for (int k = 0; k < G::MT / 4; ++k) {
-          const f32x4 x = *reinterpret_cast<const f32x4*>(src + 4 * k);
+          const f32x4 x = src[k * kWave];
 #pragma unroll
           for (int j = 0; j < 4; ++j) v[4 * k + j] += x[j];
         }
