@@ -22,6 +22,10 @@ template <int KV, int D, bool BF16>
 __global__ void __launch_bounds__(256) kv_store_kernel(StoreLaunch a) {
   constexpr int E = KV == KV_F16 ? 2 : 1;
   constexpr int CH = D / 8;                       // 8-dim chunks per head
+  // every launch argument in one round of scalar loads, ahead of the first branch
+  asm volatile("" ::"s"(a.k), "s"(a.v), "s"(a.k_stride), "s"(a.v_stride), "s"(a.slots), "s"(a.num_tokens),
+               "s"(a.k_cache), "s"(a.v_cache), "s"(a.num_pages), "s"(a.hkv), "s"(a.k_scale), "s"(a.v_scale),
+               "s"(gridDim.x), "s"(blockDim.x));
   // the host guarantees num_tokens * hkv * CH < 2^31
   const int32_t units = (int32_t)(a.num_tokens * a.hkv * CH);
   const int64_t limit = a.num_pages * kPage;
@@ -37,6 +41,7 @@ __global__ void __launch_bounds__(256) kv_store_kernel(StoreLaunch a) {
     const u32x4 kr = load16(ksrc);
     const u32x4 vr = load16(vsrc);
     const int64_t slot = a.slots[t];
+    asm volatile("" ::"v"(kr), "v"(vr), "v"(slot));   // all three in flight before the first wait
     if (slot < 0 || slot >= limit) continue;
     const int64_t page = slot >> 4;
     const int tp = (int)(slot & 15);

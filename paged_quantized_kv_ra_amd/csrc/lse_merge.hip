@@ -23,6 +23,8 @@ template <int D, int OUT>
 __global__ void __launch_bounds__(256) lse_merge_kernel(MergeLaunch a) {
   constexpr int PER = D / 64;
   constexpr int BATCH = 16;                    // partial rows in flight per lane
+  // every launch argument in one round of scalar loads, ahead of the first branch
+  asm volatile("" ::"s"(a.part_out), "s"(a.part_lse), "s"(a.parts), "s"(a.rows), "s"(a.out), "s"(a.lse));
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= a.rows) return;
   const int lane = threadIdx.x & 63;
