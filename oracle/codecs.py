@@ -27,13 +27,20 @@ Readings taken where the pages are silent:
 * INT8: round half to even, clamp to [-127, 127], NaN -> 0; -128 is never
   written;
 * FP16 cache: IEEE round-to-nearest-even cast of the fp32 value, no scale;
-* dequantise = ``fp32(decoded code) * fp32(scale)``, one fp32 rounding.
+* dequantise = ``fp32(decoded code) * fp32(scale)``, one fp32 rounding;
+* INT8 with runtime scales per token and head ('int8_tok', ReVolta README,
+  "Weight and KV formats", INT8 KV): each (token, head) row of D values gets
+  its own fp32 scale ``fp32(max_d |x|) / fp32(127)`` and is then quantised
+  exactly like per-layer INT8 with that scale; a row of zeros has scale 0
+  and codes 0.
 
 Pins (tests/test_oracle_codecs.py): the OCP E4M3 reference values, an
 exhaustive 256-code round trip, every midpoint between adjacent codes and
 one fp32 ulp either side of it, saturation, a library cross-check against
 torch's float8_e4m3fn cast on in-range values, explicit INT8 tie tables and
-a nearest-integer property check, FP16 tie and overflow cases.
+a nearest-integer property check, FP16 tie and overflow cases; for the
+per-token INT8 scales a hand-worked row, the max element at +-127, the
+half-step error bound and the zero row.
 """
 import numpy as np
 
@@ -150,7 +157,7 @@ def quantize(x32, kv_dtype, scale):
         return e4m3_encode(y)
     if kv_dtype == "int8":
         return int8_encode(y)
-    raise ValueError(kv_dtype)
+    raise ValueError(kv_dtype)   # 'int8_tok' has per-row scales: quantize_per_token
 
 
 def dequantize(codes, kv_dtype, scale):
@@ -165,6 +172,39 @@ def dequantize(codes, kv_dtype, scale):
     else:
         raise ValueError(kv_dtype)
     return (v * s).astype(_F32)
+
+
+def token_scales(x32):
+    """Per-row INT8 scales over the last axis: fp32(max |x|) / fp32(127)."""
+    amax = np.max(np.abs(np.asarray(x32, dtype=_F32)), axis=-1)
+    return (amax / _F32(INT8_MAX)).astype(_F32)
+
+
+def quantize_per_token(x32):
+    """('int8_tok') -> (int8 codes, fp32 scales): every row of the last axis
+    is quantised with its own scale; a zero row (scale 0) gets codes 0."""
+    x32 = np.asarray(x32, dtype=_F32)
+    s = token_scales(x32)
+    safe = np.where(s > 0, s, _F32(1))
+    y = (x32 / safe[..., None]).astype(_F32)
+    codes = int8_encode(y)
+    codes[s == 0] = 0
+    return codes, s
+
+
+def dequantize_per_token(codes, scales):
+    """fp32(code) * fp32(row scale), one fp32 rounding."""
+    v = np.asarray(codes, dtype=np.int8).astype(_F32)
+    return (v * np.asarray(scales, dtype=_F32)[..., None]).astype(_F32)
+
+
+def roundtrip(x32, kv_dtype, scale=None):
+    """What the cache holds for fp32 values, dequantised exactly (fp32):
+    per-layer formats use ``scale``; 'int8_tok' uses per-row scales."""
+    if kv_dtype == "int8_tok":
+        codes, s = quantize_per_token(x32)
+        return dequantize_per_token(codes, s)
+    return dequantize(quantize(x32, kv_dtype, scale), kv_dtype, scale)
 
 
 def code_nbytes(kv_dtype):

@@ -25,6 +25,10 @@ Inside a block, with ``b`` the byte position computed below,
 * V element (t, d):  lane = 16 * (t // 4) + d // (D/16),
                      b = ((d % (D/16)) * 4 + t % 4) * e
 
+INT8 with per-token scales ('int8_tok') stores its codes exactly like INT8
+and, beside each cache, a plane of fp32 scales ``[num_pages][Hkv][16]``:
+the scale of (slot, head) is float number ``(page * Hkv + head) * 16 + t``.
+
 Scatter (the method's store step): for new token n with slot >= 0,
 ``cache[slot // 16][h][slot % 16][:] = code(n, h, :)``; bytes of tokens not
 stored keep their previous content; slot < 0 means "skip".
@@ -106,9 +110,30 @@ def gather(cache_bytes, slots, which, num_kv_heads, D, kv_dtype):
     raw = np.ascontiguousarray(raw)
     if kv_dtype == "f16":
         return raw.view(np.float16).reshape(raw.shape[:-1])
-    if kv_dtype == "int8":
+    if kv_dtype in ("int8", "int8_tok"):
         return raw.view(np.int8).reshape(raw.shape[:-1])
     return raw.reshape(raw.shape[:-1])
+
+
+def scale_index(slots, num_kv_heads):
+    """int64[n, Hkv]: float index of each (slot, head) scale in a scale plane."""
+    slots = np.asarray(slots, dtype=np.int64)
+    heads = np.arange(num_kv_heads, dtype=np.int64)
+    return ((slots // PAGE)[:, None] * num_kv_heads + heads[None, :]) * PAGE + (slots % PAGE)[:, None]
+
+
+def scatter_scales(plane, scales, slots, num_kv_heads):
+    """Write scales [n][Hkv] into a flat fp32 scale plane; slot < 0 skipped."""
+    out = np.array(plane, dtype=np.float32, copy=True).reshape(-1)
+    slots = np.asarray(slots, dtype=np.int64)
+    keep = slots >= 0
+    out[scale_index(slots[keep], num_kv_heads)] = np.asarray(scales, dtype=np.float32)[keep]
+    return out
+
+
+def gather_scales(plane, slots, num_kv_heads):
+    """Read scales [n][Hkv] for the given slots back from a flat scale plane."""
+    return np.asarray(plane, dtype=np.float32).reshape(-1)[scale_index(slots, num_kv_heads)]
 
 
 def slots_for_sequence(block_table_row, ctx):

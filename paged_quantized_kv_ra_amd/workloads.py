@@ -66,7 +66,7 @@ class Workload:
     num_q_heads: int
     num_kv_heads: int
     head_dim: int
-    kv_dtype: str                 # 'f16' | 'e4m3' | 'int8'
+    kv_dtype: str                 # 'f16' | 'e4m3' | 'int8' | 'int8_tok' (INT8, scale per token and head)
     q_dtype: str                  # 'f16' | 'bf16' (bf16 as uint16 bits)
     src_dtype: str                # dtype of new K/V handed to the store
     ctx: np.ndarray               # int32[B], includes this step's q_len
@@ -132,7 +132,10 @@ class Workload:
         return tot
 
     def kv_bytes_attended(self):
-        return self.attended_keys() * 2 * self.num_kv_heads * self.head_dim * self.elem_bytes
+        """K and V bytes of the visible tokens (codes, plus the fp32 K and V
+        scales of every token and head for per-token INT8)."""
+        per_head = self.head_dim * self.elem_bytes + (4 if self.kv_dtype == "int8_tok" else 0)
+        return self.attended_keys() * 2 * self.num_kv_heads * per_head
 
     def unique_pages_attended(self):
         """Distinct physical pages touched (shared prefix pages counted once)."""
@@ -223,9 +226,9 @@ def build(name, seed, *, ctx, q_len, num_q_heads, num_kv_heads, head_dim,
     elif kv_dtype == "int8":
         k_scale = float(_absmax_f32(tokens_k, src_dtype) / np.float32(127.0))
         v_scale = float(_absmax_f32(tokens_v, src_dtype) / np.float32(127.0))
-    else:
+    else:                         # FP16 (no scale) or per-token INT8 (scales made by the store)
         k_scale = v_scale = 1.0
-    sentinel = {"f16": 0x7E00, "e4m3": 0x7F, "int8": 0x80}[kv_dtype]
+    sentinel = {"f16": 0x7E00, "e4m3": 0x7F, "int8": 0x80, "int8_tok": 0x80}[kv_dtype]
     qsl = np.zeros(B + 1, dtype=np.int64)
     qsl[1:] = np.cumsum(q_len)
     return Workload(
@@ -274,6 +277,14 @@ def decode_fp8_32k():
                  pool_pages=16384)
 
 
+def verify_int8tok_32k():
+    """The 8 x 32K verify shape with INT8 KV scaled per token and head at
+    runtime (ReVolta README, "Weight and KV formats", INT8 KV)."""
+    return build("verify_int8tok_8x32k_q5", 6, ctx=[32 * K] * 8, q_len=5, num_q_heads=16,
+                 num_kv_heads=2, head_dim=128, kv_dtype="int8_tok", q_dtype="f16",
+                 pool_pages=16384)
+
+
 def prefix_int8_256k():
     """4 x 256K sharing the first 192K tokens' pages, INT8 KV, q_len 5."""
     return build("prefix_int8_4x256k_shared192k_q5", 3, ctx=[256 * K] * 4, q_len=5,
@@ -302,6 +313,7 @@ BENCH_WORKLOADS = {
     "batch8_decode": batch8_decode,
     "verify_fp8_32k": verify_fp8_32k,
     "decode_fp8_32k": decode_fp8_32k,
+    "verify_int8tok_32k": verify_int8tok_32k,
     "prefix_int8_256k": prefix_int8_256k,
     "split_fp8_512k": split_fp8_512k,
     "split_fp8_512k_sliding": split_fp8_512k_sliding,

@@ -189,3 +189,40 @@ def test_quantize_dequantize_error_bound(kv):
         normal = np.abs(x) >= 2.0 ** -6 * s
         assert np.all(err[normal] <= np.abs(x[normal]) * 2.0 ** -4 * (1 + 1e-6))
         assert np.all(err[~normal] <= 2.0 ** -10 * s * (1 + 1e-6))
+
+
+# ---- INT8 with runtime scales per token and head ('int8_tok')
+
+def test_int8_token_hand_worked_row():
+    """max |x| = 2.54 -> scale = fp32(2.54) / 127 (about 0.02); the other
+    values sit far from any rounding boundary: 1.0 -> 50, -0.5 -> -25,
+    0.26 -> 13, -2.54 -> -127, 0 -> 0."""
+    x = np.array([[1.0, -0.5, 0.26, -2.54, 0.0, 2.0]], dtype=np.float32)
+    codes, s = codecs.quantize_per_token(x)
+    assert s.dtype == np.float32 and s[0] == np.float32(np.float32(2.54) / np.float32(127))
+    assert codes.tolist() == [[50, -25, 13, -127, 0, 100]]
+
+
+def test_int8_token_max_element_codes_127_and_half_step_bound():
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal((300, 4, 128)) * rng.uniform(1e-3, 50.0, (300, 4, 1))).astype(np.float32)
+    codes, s = codecs.quantize_per_token(x)
+    assert s.shape == (300, 4)
+    idx = np.argmax(np.abs(x), axis=-1)
+    top = np.take_along_axis(codes, idx[..., None], axis=-1)[..., 0].astype(np.int64)
+    sign = np.sign(np.take_along_axis(x, idx[..., None], axis=-1)[..., 0])
+    assert np.all(top == 127 * sign)
+    assert codes.min() >= -127 and codes.max() <= 127
+    err = np.abs(codecs.dequantize_per_token(codes, s).astype(np.float64) - x.astype(np.float64))
+    # half a quantisation step, plus the fp32 roundings of the quotient and the product
+    assert np.all(err <= s[..., None].astype(np.float64) * (0.5 + 1e-4))
+
+
+def test_int8_token_zero_row_and_roundtrip_dispatch():
+    x = np.zeros((2, 1, 8), dtype=np.float32)
+    x[1, 0, 3] = -4.0
+    codes, s = codecs.quantize_per_token(x)
+    assert s[0, 0] == 0.0 and np.all(codes[0] == 0)
+    assert codes[1, 0, 3] == -127 and np.all(np.delete(codes[1, 0], 3) == 0)
+    r = codecs.roundtrip(x, "int8_tok")
+    assert r[1, 0, 3] == np.float32(-127) * s[1, 0] and np.all(r[0] == 0)

@@ -84,3 +84,20 @@ def test_slots_for_sequence():
     row = np.array([7, 2, 9])
     s = layout.slots_for_sequence(row, 35)
     assert s[0] == 112 and s[15] == 127 and s[16] == 32 and s[34] == 146
+
+
+def test_scale_plane_offsets_and_round_trip():
+    # hand-worked: Hkv = 2, slot 37 = page 2, token 5 -> (2 * 2 + h) * 16 + 5
+    assert layout.scale_index([37], 2).tolist() == [[69, 85]]
+    rng = np.random.default_rng(5)
+    pages, hkv = 12, 2
+    slots = rng.permutation(pages * 16)[:100].astype(np.int64)
+    slots[::9] = -1
+    sc = rng.standard_normal((100, hkv)).astype(np.float32)
+    plane0 = np.full(pages * hkv * 16, np.float32(7.0))
+    plane = layout.scatter_scales(plane0, sc, slots, hkv)
+    keep = slots >= 0
+    np.testing.assert_array_equal(layout.gather_scales(plane, slots[keep], hkv), sc[keep])
+    touched = np.zeros(plane.size, bool)
+    touched[layout.scale_index(slots[keep], hkv).ravel()] = True
+    assert np.all(plane[~touched] == 7.0)
