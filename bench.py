@@ -88,15 +88,22 @@ class Step:
         # one pool filled through the store, then cloned
         k0 = P.new_cache(w.num_pages, hkv, D, w.kv_dtype, dev, fill=w.cache_sentinel)
         v0 = P.new_cache(w.num_pages, hkv, D, w.kv_dtype, dev, fill=w.cache_sentinel)
+        ks0 = vs0 = None
+        if w.kv_dtype == "int8_tok":      # per-token scale planes beside the caches
+            ks0 = P.new_scale_plane(w.num_pages, hkv, dev)
+            vs0 = P.new_scale_plane(w.num_pages, hkv, dev)
         U = w.tokens_k.shape[0]
         chunk = 1 << 18
         for lo in range(0, U, chunk):
             hi = min(U, lo + chunk)
             P.kv_store(self._src(w.tokens_k[lo:hi]), self._src(w.tokens_v[lo:hi]),
-                       torch.from_numpy(w.token_slots[lo:hi]).to(dev), k0, v0, w.kv_dtype, w.k_scale, w.v_scale)
-        pool_bytes = 2 * k0.numel() * k0.element_size()
+                       torch.from_numpy(w.token_slots[lo:hi]).to(dev), k0, v0, w.kv_dtype, w.k_scale, w.v_scale,
+                       k_scales=ks0, v_scales=vs0)
+        pool_bytes = 2 * k0.numel() * k0.element_size() + (2 * ks0.numel() * 4 if ks0 is not None else 0)
         self.copies = max(1, -(-POOL_ROTATION_BYTES // pool_bytes))
-        self.pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(self.copies - 1)]
+        clone = (lambda t: None if t is None else t.clone())
+        self.pools = [(k0, v0, ks0, vs0)] + [(k0.clone(), v0.clone(), clone(ks0), clone(vs0))
+                                             for _ in range(self.copies - 1)]
         torch.cuda.synchronize()
         # this step's new tokens: the last q_len positions of every sequence
         rows = w.new_token_rows()
@@ -111,10 +118,10 @@ class Step:
         self.out = torch.empty_like(self.q)
         self.lse = torch.empty((T, hq), dtype=torch.float32, device=dev)
         self.args = []
-        for k, v in self.pools:
+        for k, v, ks, vs in self.pools:
             a = L._attn_args(self.q, k, v, self.bt, self.ctx, self.qsl, w.kv_dtype, w.k_scale, w.v_scale,
                              w.softmax_scale, w.max_q_len, int(w.q_len.min()), w.max_context_len,
-                             w.window_left, w.num_sinks, w.num_splits, hkv)
+                             w.window_left, w.num_sinks, w.num_splits, hkv, ks, vs)
             self.args.append(a)
         self.slots, po_n, _ = L.paged_attn_workspace(self.args[0])
         self.po = torch.empty((self.slots, T, hq, D), dtype=torch.float32, device=dev)
@@ -148,12 +155,18 @@ class Step:
     def run(self, i, stream, ev=None):
         """Enqueue step i: store, attention (between the two events), merge."""
         w, lib, L = self.w, self.lib, self.L
-        k, v = self.pools[i % self.copies]
+        k, v, ks, vs = self.pools[i % self.copies]
         s = ctypes.c_void_p(stream)
-        st = lib.ra_kv_store(self.k_new.data_ptr(), self.v_new.data_ptr(), L.RA_F16, self.k_new.stride(0),
-                             self.v_new.stride(0), self.slots_new.data_ptr(), self.k_new.shape[0], k.data_ptr(),
-                             v.data_ptr(), self.kv_code, w.num_pages, w.num_kv_heads, w.head_dim, 16,
-                             w.k_scale, w.v_scale, s)
+        if ks is not None:
+            st = lib.ra_kv_store_int8_token(self.k_new.data_ptr(), self.v_new.data_ptr(), L.RA_F16,
+                                            self.k_new.stride(0), self.v_new.stride(0), self.slots_new.data_ptr(),
+                                            self.k_new.shape[0], k.data_ptr(), v.data_ptr(), ks.data_ptr(),
+                                            vs.data_ptr(), w.num_pages, w.num_kv_heads, w.head_dim, 16, s)
+        else:
+            st = lib.ra_kv_store(self.k_new.data_ptr(), self.v_new.data_ptr(), L.RA_F16, self.k_new.stride(0),
+                                 self.v_new.stride(0), self.slots_new.data_ptr(), self.k_new.shape[0],
+                                 k.data_ptr(), v.data_ptr(), self.kv_code, w.num_pages, w.num_kv_heads,
+                                 w.head_dim, 16, w.k_scale, w.v_scale, s)
         if ev is not None:
             ev[0].record()
         st |= lib.ra_paged_attn(ctypes.byref(self.args[i % self.copies]), s)
@@ -167,7 +180,8 @@ class Step:
 
 def algorithmic_bytes(w):
     """HBM bytes one attention launch must move: the visible KV tokens' codes
-    (2 * Hkv * D * e per token), the block-table entries of the visited pages
+    (2 * Hkv * D * e per token, plus 2 * Hkv * 4 B of scales for per-token
+    INT8), the block-table entries of the visited pages
     (4 B per 16 tokens per sequence) and the queries."""
     kv = w.kv_bytes_attended()
     bt = 4 * sum(-(-int(c) // 16) for c in w.ctx)

@@ -64,6 +64,15 @@
  *   INT8: round half to even, clamp to [-127, 127], NaN -> 0;
  *   FP16 cache: IEEE round-to-nearest-even of fp32(x), no scale.
  *   Dequantised value = fp32(decode(code)) * fp32(scale).
+ *
+ * INT8 with runtime scales per token and head (RA_KV_INT8_TOKEN; ReVolta
+ * README, "Weight and KV formats", INT8 KV): each (token, head) row of
+ * head_dim values gets scale = fp32(max |x|) / fp32(127), correctly rounded,
+ * and is quantised as INT8 above with that scale (a row of zeros: scale 0,
+ * codes 0).  The codes use the INT8 layout; the scales live in two fp32
+ * planes beside the caches, k_scales and v_scales [num_pages][num_kv_heads][16],
+ * the scale of (slot, head) at float index (page * num_kv_heads + head) * 16
+ * + slot % 16.
  */
 #ifndef RA_KV_H_
 #define RA_KV_H_
@@ -75,7 +84,7 @@
 extern "C" {
 #endif
 
-#define RA_KV_ABI_VERSION 1
+#define RA_KV_ABI_VERSION 2
 #define RA_KV_LAYOUT_ID 1
 #define RA_KV_PAGE_SIZE 16
 #define RA_KV_MAX_SPLITS 4096
@@ -94,7 +103,7 @@ enum {
 enum { RA_F16 = 1, RA_BF16 = 2, RA_F32 = 3 };
 
 /* KV cache element formats. */
-enum { RA_KV_F16 = 1, RA_KV_FP8_E4M3 = 2, RA_KV_INT8 = 3 };
+enum { RA_KV_F16 = 1, RA_KV_FP8_E4M3 = 2, RA_KV_INT8 = 3, RA_KV_INT8_TOKEN = 4 };
 
 /*
  * ra_kv_store -- quantise new K/V rows and scatter them into the paged caches.
@@ -122,6 +131,21 @@ int32_t ra_kv_store(const void* k, const void* v, int32_t src_dtype,
                     void* k_cache, void* v_cache, int32_t kv_dtype,
                     int64_t num_pages, int32_t num_kv_heads, int32_t head_dim,
                     int32_t page_size, float k_scale, float v_scale, void* stream);
+
+/*
+ * ra_kv_store_int8_token -- ra_kv_store for RA_KV_INT8_TOKEN caches: quantise
+ * new K/V rows with their own per-(token, head) scales (layout and rule above),
+ * scatter the codes into k_cache / v_cache and the scales into k_scales /
+ * v_scales.  Arguments as ra_kv_store, with the scale planes (fp32,
+ * num_pages * num_kv_heads * 16 each, 16-byte aligned) in place of the
+ * per-layer scales.  Non-finite inputs give unspecified codes.
+ */
+int32_t ra_kv_store_int8_token(const void* k, const void* v, int32_t src_dtype,
+                               int64_t k_token_stride, int64_t v_token_stride,
+                               const int64_t* slot_mapping, int64_t num_tokens,
+                               void* k_cache, void* v_cache, float* k_scales, float* v_scales,
+                               int64_t num_pages, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t page_size, void* stream);
 
 /*
  * Arguments of ra_paged_attn.  Set struct_size = sizeof(ra_attn_args).
@@ -177,6 +201,8 @@ typedef struct ra_attn_args {
   float* partial_out;              /* workspace, see above                       */
   float* partial_lse;
   int32_t partial_slots;           /* slots the partial buffers hold             */
+  const float* k_scales;           /* RA_KV_INT8_TOKEN: scale planes (layout     */
+  const float* v_scales;           /* above); ignored by the other formats       */
 } ra_attn_args;
 
 /*
@@ -184,7 +210,9 @@ typedef struct ra_attn_args {
  * Argument meaning, layouts and the split rule are given with ra_attn_args.
  * Host checks: non-null pointers; 16-byte aligned q, out and caches;
  * Hq % Hkv == 0; head_dim in {64, 128}; page_size == 16; known dtypes; finite
- * positive scales for E4M3 / INT8; 1 <= max_q_len; max_context_len <=
+ * positive scales for E4M3 / INT8; non-null, 16-byte aligned scale planes for
+ * RA_KV_INT8_TOKEN (k_scale / v_scale are then ignored); 1 <= max_q_len;
+ * max_context_len <=
  * block_table_stride * 16; num_splits in [0, RA_KV_MAX_SPLITS]; partial
  * buffers present and partial_slots >= the slots needed when more than one
  * slot is used.
@@ -223,11 +251,13 @@ int32_t ra_lse_merge(const float* partial_out, const float* partial_lse,
  * ra_kv_gather_dequant -- (test and debugging aid) read one sequence's K or V
  * back through its block-table row and dequantise it exactly.
  * which: 0 = K cache, 1 = V cache.  out [ctx][num_kv_heads][head_dim] fp32 =
- * fp32(decode(code)) * scale (FP16 caches: the fp16 value, scale ignored).
+ * fp32(decode(code)) * scale (FP16 caches: the fp16 value, scale ignored;
+ * RA_KV_INT8_TOKEN: the (slot, head) scale from the plane `scales`, which is
+ * ignored, and may be NULL, for the other formats).
  * Positions whose page id is outside [0, num_pages) are written as NaN.
  */
 int32_t ra_kv_gather_dequant(const void* cache, int32_t which, int32_t kv_dtype,
-                             float scale, const int32_t* block_table_row,
+                             float scale, const float* scales, const int32_t* block_table_row,
                              int32_t ctx, int64_t num_pages, int32_t num_kv_heads,
                              int32_t head_dim, float* out, void* stream);
 

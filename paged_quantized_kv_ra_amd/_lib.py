@@ -20,8 +20,8 @@ LIB_PATH = os.environ.get("RA_KV_LIB") or os.path.join(os.path.dirname(os.path.a
 
 RA_OK, RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED, RA_ERR_MISALIGNED, RA_ERR_WORKSPACE, RA_ERR_HIP = range(6)
 RA_F16, RA_BF16, RA_F32 = 1, 2, 3
-RA_KV_F16, RA_KV_FP8_E4M3, RA_KV_INT8 = 1, 2, 3
-KV_CODES = {"f16": RA_KV_F16, "e4m3": RA_KV_FP8_E4M3, "int8": RA_KV_INT8}
+RA_KV_F16, RA_KV_FP8_E4M3, RA_KV_INT8, RA_KV_INT8_TOKEN = 1, 2, 3, 4
+KV_CODES = {"f16": RA_KV_F16, "e4m3": RA_KV_FP8_E4M3, "int8": RA_KV_INT8, "int8_tok": RA_KV_INT8_TOKEN}
 PAGE = 16
 
 _c = ctypes
@@ -62,6 +62,8 @@ class AttnArgs(_c.Structure):
         ("partial_out", _vp),
         ("partial_lse", _vp),
         ("partial_slots", _c.c_int32),
+        ("k_scales", _vp),
+        ("v_scales", _vp),
     ]
 
 
@@ -69,11 +71,13 @@ EXPORTED = {
     "ra_kv_store": (_c.c_int32, [_vp, _vp, _c.c_int32, _c.c_int64, _c.c_int64, _vp, _c.c_int64, _vp, _vp,
                                  _c.c_int32, _c.c_int64, _c.c_int32, _c.c_int32, _c.c_int32, _c.c_float,
                                  _c.c_float, _vp]),
+    "ra_kv_store_int8_token": (_c.c_int32, [_vp, _vp, _c.c_int32, _c.c_int64, _c.c_int64, _vp, _c.c_int64, _vp,
+                                            _vp, _vp, _vp, _c.c_int64, _c.c_int32, _c.c_int32, _c.c_int32, _vp]),
     "ra_paged_attn": (_c.c_int32, [_c.POINTER(AttnArgs), _vp]),
     "ra_paged_attn_workspace": (_c.c_int32, [_c.POINTER(AttnArgs), _c.POINTER(_c.c_int32),
                                              _c.POINTER(_c.c_int64), _c.POINTER(_c.c_int64)]),
     "ra_lse_merge": (_c.c_int32, [_vp, _vp, _c.c_int32, _c.c_int64, _c.c_int32, _vp, _c.c_int32, _vp, _vp]),
-    "ra_kv_gather_dequant": (_c.c_int32, [_vp, _c.c_int32, _c.c_int32, _c.c_float, _vp, _c.c_int32,
+    "ra_kv_gather_dequant": (_c.c_int32, [_vp, _c.c_int32, _c.c_int32, _c.c_float, _vp, _vp, _c.c_int32,
                                           _c.c_int64, _c.c_int32, _c.c_int32, _vp, _vp]),
     "ra_last_error": (_c.c_char_p, []),
     "ra_abi_version": (_c.c_int32, []),
@@ -138,6 +142,11 @@ def new_cache(num_pages, num_kv_heads, head_dim, kv_dtype, device="cuda", fill=N
     return t
 
 
+def new_scale_plane(num_pages, num_kv_heads, device="cuda", fill=float("nan")):
+    """Allocate one per-token INT8 scale plane [num_pages][num_kv_heads][16] fp32."""
+    return torch.full((num_pages, num_kv_heads, PAGE), fill, dtype=torch.float32, device=device)
+
+
 def _src_code(t):
     if t.dtype == torch.float16:
         return RA_F16
@@ -146,12 +155,20 @@ def _src_code(t):
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def kv_store(k, v, slot_mapping, k_cache, v_cache, kv_dtype, k_scale=1.0, v_scale=1.0, stream=None):
-    """Quantise k, v [T][Hkv][D] and scatter them into the caches at slot_mapping."""
+def kv_store(k, v, slot_mapping, k_cache, v_cache, kv_dtype, k_scale=1.0, v_scale=1.0, stream=None,
+             k_scales=None, v_scales=None):
+    """Quantise k, v [T][Hkv][D] and scatter them into the caches at slot_mapping
+    (per-token INT8: also their scales into the k_scales / v_scales planes)."""
     T, hkv, D = k.shape
     assert v.shape == k.shape and k.stride(2) == 1 and k.stride(1) == D and v.stride(2) == 1 and v.stride(1) == D
     assert slot_mapping.dtype == torch.int64 and slot_mapping.numel() == T
     num_pages = k_cache.shape[0]
+    if kv_dtype == "int8_tok":
+        _check(load_library().ra_kv_store_int8_token(
+            _ptr(k), _ptr(v), _src_code(k), k.stride(0), v.stride(0), _ptr(slot_mapping), T,
+            _ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales), num_pages, hkv, D, PAGE,
+            _stream(stream)))
+        return
     _check(load_library().ra_kv_store(
         _ptr(k), _ptr(v), _src_code(k), k.stride(0), v.stride(0), _ptr(slot_mapping), T,
         _ptr(k_cache), _ptr(v_cache), KV_CODES[kv_dtype], num_pages, hkv, D, PAGE,
@@ -160,7 +177,7 @@ def kv_store(k, v, slot_mapping, k_cache, v_cache, kv_dtype, k_scale=1.0, v_scal
 
 def _attn_args(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, kv_dtype, k_scale,
                v_scale, softmax_scale, max_q_len, min_q_len, max_context_len, window_left, num_sinks,
-               num_splits, num_kv_heads):
+               num_splits, num_kv_heads, k_scales=None, v_scales=None):
     T, hq, D = q.shape
     a = AttnArgs()
     a.struct_size = _c.sizeof(AttnArgs)
@@ -189,6 +206,8 @@ def _attn_args(q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
     a.window_left = int(window_left)
     a.num_sinks = int(num_sinks)
     a.num_splits = int(num_splits)
+    a.k_scales = None if k_scales is None else k_scales.data_ptr()
+    a.v_scales = None if v_scales is None else v_scales.data_ptr()
     return a
 
 
@@ -203,7 +222,7 @@ def paged_attn_workspace(args):
 def paged_attn(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, *, kv_dtype,
                max_q_len, max_context_len, k_scale=1.0, v_scale=1.0, softmax_scale=None, min_q_len=0,
                window_left=-1, num_sinks=0, num_splits=0, out=None, lse=None, partials_only=False,
-               workspace=None, stream=None):
+               workspace=None, stream=None, k_scales=None, v_scales=None):
     """Attention of the query blocks over the paged caches.
 
     q [total_q][Hq][D] fp16/bf16; block_tables int32 [B][stride];
@@ -215,7 +234,7 @@ def paged_attn(q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
     hkv = k_cache.shape[1]
     a = _attn_args(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, kv_dtype, k_scale,
                    v_scale, softmax_scale, max_q_len, min_q_len, max_context_len, window_left, num_sinks,
-                   num_splits, hkv)
+                   num_splits, hkv, k_scales, v_scales)
     if not partials_only:
         if out is None:
             out = torch.empty_like(q)
@@ -255,11 +274,11 @@ def lse_merge(partial_out, partial_lse, out_dtype=torch.float32, out=None, lse=N
     return out, lse
 
 
-def kv_gather_dequant(cache, which, kv_dtype, scale, block_table_row, ctx, head_dim, stream=None):
+def kv_gather_dequant(cache, which, kv_dtype, scale, block_table_row, ctx, head_dim, stream=None, scales=None):
     """Exact dequantised [ctx][Hkv][D] fp32 read-back of one sequence's K (which=0) or V (1)."""
     hkv = cache.shape[1]
     out = torch.empty((ctx, hkv, head_dim), dtype=torch.float32, device=cache.device)
-    _check(load_library().ra_kv_gather_dequant(_ptr(cache), which, KV_CODES[kv_dtype], float(scale),
+    _check(load_library().ra_kv_gather_dequant(_ptr(cache), which, KV_CODES[kv_dtype], float(scale), _ptr(scales),
                                                _ptr(block_table_row), ctx, cache.shape[0], hkv, head_dim,
                                                _ptr(out), _stream(stream)))
     return out

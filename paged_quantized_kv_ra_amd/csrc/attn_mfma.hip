@@ -52,12 +52,16 @@ struct Geo {
   // 2 .. 8 pages; NRING - 1 pages are in flight while one computes
   static constexpr int NRING_RAW = RA_MFMA_RING_KIB / NSL;
   static constexpr int NRING = NRING_RAW > 8 ? 8 : (NRING_RAW < 2 ? 2 : NRING_RAW);
+  // vector-memory operations per page: the slabs, plus one load of the
+  // page's 16 K and 16 V scales for per-token INT8
+  static constexpr int OPS = NSL + (KV == KV_I8T ? 1 : 0);
 };
 
 template <int KV, int D>
 struct PageRegs {
   u32x4 k[Geo<KV, D>::SLABS];
   u32x4 v[Geo<KV, D>::SLABS];
+  f32x4 ks, vs;   // per-token INT8: the K and V scales of the lane's 4 tokens
 };
 
 // Page ids of the pages one wave visits, staged 64 at a time in LDS by the
@@ -108,12 +112,20 @@ __device__ __forceinline__ int32_t ring_page_id(IdRing& r, int32_t (*sm_id)[64],
 // straight into the LDS ring slot `ring`: one global_load_lds_dwordx4 per 1 KiB
 // slab, lane L writing bytes L*16 .. L*16+15 of the slab, the lane order the
 // cache layout has in HBM.
+// Per-token INT8 adds one load of the (page, head)'s 16 K scales (lanes 0-15)
+// and 16 V scales (lanes 16-31) into the slot's 128-byte scale area `scl`.
 template <int KV, int D>
-__device__ __forceinline__ void issue_page(uint8_t (*ring)[kSlab], IdRing& ids, int32_t (*sm_id)[64],
+__device__ __forceinline__ void issue_page(uint8_t (*ring)[kSlab], float* scl, IdRing& ids, int32_t (*sm_id)[64],
                                            const AttnLaunch& a, const UnitPages& pg, const WaveSpan& ws,
                                            int32_t i, const int32_t* bt_row, int h, int lane, bool& bad) {
   using G = Geo<KV, D>;
   const int32_t pid = ring_page_id(ids, sm_id, a, pg, ws, bt_row, i, lane, bad);
+  if constexpr (KV == KV_I8T) {
+    if (lane < 32) {
+      const float* src = (lane < 16 ? a.k_scales : a.v_scales) + ((int64_t)pid * a.hkv + h) * kPage + (lane & 15);
+      __builtin_amdgcn_global_load_lds(src, (lds_u8*)scl, 4, 0, 0);
+    }
+  }
   const int64_t blk = ((int64_t)pid * a.hkv + h) * G::BLK;
   const uint8_t* kp = a.k_cache + blk + (uint32_t)lane * 16u;
   const uint8_t* vp = a.v_cache + blk + (uint32_t)lane * 16u;
@@ -139,12 +151,17 @@ __device__ __forceinline__ void wait_lgkmcnt0() {
 }
 
 template <int KV, int D>
-__device__ __forceinline__ void read_page(PageRegs<KV, D>& r, const uint8_t (*ring)[kSlab], uint32_t lane_off) {
+__device__ __forceinline__ void read_page(PageRegs<KV, D>& r, const uint8_t (*ring)[kSlab], const float* scl,
+                                          uint32_t lane_off, int kgrp) {
   using G = Geo<KV, D>;
 #pragma unroll
   for (int j = 0; j < G::SLABS; ++j) r.k[j] = *reinterpret_cast<const u32x4*>(ring[j] + lane_off);
 #pragma unroll
   for (int j = 0; j < G::SLABS; ++j) r.v[j] = *reinterpret_cast<const u32x4*>(ring[G::SLABS + j] + lane_off);
+  if constexpr (KV == KV_I8T) {
+    r.ks = *reinterpret_cast<const f32x4*>(scl + 4 * kgrp);
+    r.vs = *reinterpret_cast<const f32x4*>(scl + 16 + 4 * kgrp);
+  }
 }
 
 // K operand of k-step ks: the lane's token, dims kgrp * D/4 + 8 ks .. + 8.
@@ -203,6 +220,10 @@ __device__ __forceinline__ void compute_page(Acc<KV, D, NT>& acc, PageRegs<KV, D
     for (int nt = 0; nt < NT; ++nt)
       s[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qf[nt][ks], s[nt], 0, 0, 0);
   }
+  if constexpr (KV == KV_I8T) {   // per-token K scales
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) s[nt] *= r.ks;
+  }
   // ---- masks (only on pages that can hold an invisible key).  Keys past ctx
   // (stale bytes of the last page) also get their V codes zeroed so that
   // 0 * garbage cannot produce NaN.
@@ -217,6 +238,7 @@ __device__ __forceinline__ void compute_page(Acc<KV, D, NT>& acc, PageRegs<KV, D
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) s[nt][i] = key_visible(a, j, pos[nt]) ? s[nt][i] : -INFINITY;
       const bool data = j < ctx;
+      if constexpr (KV == KV_I8T) r.vs[i] = data ? r.vs[i] : 0.0f;   // the scale plane past ctx is not data
       keep8 |= data ? 0xFFu << (8 * i) : 0u;
       if (i < 2) keep_lo |= data ? 0xFFFFu << (16 * i) : 0u;
       else keep_hi |= data ? 0xFFFFu << (16 * (i - 2)) : 0u;
@@ -258,7 +280,7 @@ __device__ __forceinline__ void compute_page(Acc<KV, D, NT>& acc, PageRegs<KV, D
     for (int i = 0; i < 4; ++i) {
       const float e = __builtin_amdgcn_exp2f(fmaf(s[nt][i], c, -mc));
       ps += e;
-      pf[nt][i] = (f16)e;
+      pf[nt][i] = KV == KV_I8T ? (f16)(e * r.vs[i]) : (f16)e;   // per-token V scales ride on P
     }
     acc.l[nt] += ps;
   }
@@ -284,6 +306,8 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a,
   __shared__ __attribute__((aligned(16))) uint8_t sm_raw[kRawBytes / kSlab][kSlab];
   __shared__ f32x4 sm_ml[2][NT * 16][kWaves / 4];   // per row: the 8 waves' m (l), read as 2 x 16 B
   __shared__ int32_t sm_ids[kWaves][2][64];
+  // per-token INT8: each ring slot's 16 K and 16 V scales
+  __shared__ __attribute__((aligned(16))) float sm_scl[KV == KV_I8T ? kWaves * G::NRING * 32 : 4];
   __shared__ int32_t sm_bad[kWaves];
 
   UnitId u;
@@ -385,30 +409,32 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a,
   if (my_pages > 0) {
     constexpr int NR = G::NRING;
     uint8_t (*ring)[kSlab] = &sm_raw[wave * NR * G::NSL];
+    float* scl = &sm_scl[KV == KV_I8T ? wave * NR * 32 : 0];
     IdRing ids{sm_id[0][lane], 0};
 #pragma unroll
     for (int j = 0; j < NR; ++j)
       if (j < my_pages)
-        issue_page<KV, D>(ring + j * G::NSL, ids, sm_id, a, pg, ws, j, bt_row, u.h, lane, bad);
+        issue_page<KV, D>(ring + j * G::NSL, scl + j * 32, ids, sm_id, a, pg, ws, j, bt_row, u.h, lane, bad);
     for (int32_t i = 0; i < my_pages; i += NR) {
 #pragma unroll
       for (int j = 0; j < NR; ++j) {
         const int32_t k = i + j;
         if (k < my_pages) {
-          // page k's slabs retire before the (NR - 1) * NSL loads issued after
+          // page k's loads retire before the (NR - 1) * OPS loads issued after
           // them, unless the tail issued fewer
           if (k + NR - 1 < my_pages)
-            wait_vmcnt<(NR - 1) * G::NSL>();
+            wait_vmcnt<(NR - 1) * G::OPS>();
           else
             wait_vmcnt<0>();
           PageRegs<KV, D> r;
-          read_page<KV, D>(r, ring + j * G::NSL, lane_off);
+          read_page<KV, D>(r, ring + j * G::NSL, scl + j * 32, lane_off, kgrp);
           compute_page<KV, D, NT>(acc, r, qf, a, pg, ws.page(k), ctx, q_len, pos, kgrp, c, thr);
           // the slot's reads have returned (their values were consumed) before
           // the next load may overwrite it
           wait_lgkmcnt0();
           if (k + NR < my_pages)
-            issue_page<KV, D>(ring + j * G::NSL, ids, sm_id, a, pg, ws, k + NR, bt_row, u.h, lane, bad);
+            issue_page<KV, D>(ring + j * G::NSL, scl + j * 32, ids, sm_id, a, pg, ws, k + NR, bt_row, u.h, lane,
+                              bad);
         }
       }
     }
@@ -582,6 +608,7 @@ hipError_t launch_attn_mfma(const AttnLaunch& a, hipStream_t s) {
   switch (a.kv) {
     case KV_F16: return launch_d<KV_F16>(a, nt, row_groups, s);
     case KV_E4M3: return launch_d<KV_E4M3>(a, nt, row_groups, s);
+    case KV_I8T: return launch_d<KV_I8T>(a, nt, row_groups, s);
     default: return launch_d<KV_I8>(a, nt, row_groups, s);
   }
 }

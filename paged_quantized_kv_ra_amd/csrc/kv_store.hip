@@ -4,8 +4,9 @@
 // The KV cache is written as FP16, FP8 E4M3 or INT8 with per-layer K and V
 // scales (ReVolta README, intro list and "Weight and KV formats"; "Running
 // FP4-Local on 4 x V100 32 GB (Volta) with ReVolta", "What it takes", for the
-// per-layer target K/V scale pack), into 16-token pages ("ReVolta 0.1.3",
-// "Known issues").
+// per-layer target K/V scale pack), or as INT8 with a scale per token and head
+// computed here at store time (ReVolta README, "Weight and KV formats", INT8
+// KV), into 16-token pages ("ReVolta 0.1.3", "Known issues").
 //
 // One thread handles 8 consecutive dimensions of one (token, head): it reads
 // 16 bytes of K and 16 of V, quantises with a correctly rounded fp32 divide,
@@ -25,7 +26,7 @@ __global__ void __launch_bounds__(256) kv_store_kernel(StoreLaunch a) {
   // every launch argument in one round of scalar loads, ahead of the first branch
   asm volatile("" ::"s"(a.k), "s"(a.v), "s"(a.k_stride), "s"(a.v_stride), "s"(a.slots), "s"(a.num_tokens),
                "s"(a.k_cache), "s"(a.v_cache), "s"(a.num_pages), "s"(a.hkv), "s"(a.k_scale), "s"(a.v_scale),
-               "s"(gridDim.x), "s"(blockDim.x));
+               "s"(gridDim.x), "s"(blockDim.x), "s"(a.k_scales), "s"(a.v_scales));
   // the host guarantees num_tokens * hkv * CH < 2^31
   const int32_t units = (int32_t)(a.num_tokens * a.hkv * CH);
   const int64_t limit = a.num_pages * kPage;
@@ -62,6 +63,29 @@ __global__ void __launch_bounds__(256) kv_store_kernel(StoreLaunch a) {
     uint8_t* kc = reinterpret_cast<uint8_t*>(a.k_cache) + blk;
     uint8_t* vc = reinterpret_cast<uint8_t*>(a.v_cache) + blk;
 
+    // per-token INT8: the (token, head) row's scale is max |x| / 127 over its
+    // CH threads (consecutive lanes of one wave, all active or all skipped)
+    float ks = a.k_scale, vs = a.v_scale;
+    if constexpr (KV == KV_I8T) {
+      float km = 0.0f, vm = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        km = fmaxf(km, fabsf(kf[i]));
+        vm = fmaxf(vm, fabsf(vf[i]));
+      }
+#pragma unroll
+      for (int o = 1; o < CH; o <<= 1) {
+        km = fmaxf(km, __shfl_xor(km, o));
+        vm = fmaxf(vm, __shfl_xor(vm, o));
+      }
+      ks = km / 127.0f;   // correctly rounded (built with -fhip-fp32-correctly-rounded-divide-sqrt)
+      vs = vm / 127.0f;
+      if (c == 0) {
+        const int64_t si = (page * a.hkv + h) * kPage + tp;
+        a.k_scales[si] = ks;
+        a.v_scales[si] = vs;
+      }
+    }
     uint32_t kcode[8], vcode[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -71,9 +95,12 @@ __global__ void __launch_bounds__(256) kv_store_kernel(StoreLaunch a) {
       } else if constexpr (KV == KV_E4M3) {
         kcode[i] = e4m3_encode(kf[i] / a.k_scale);
         vcode[i] = e4m3_encode(vf[i] / a.v_scale);
-      } else {
-        kcode[i] = (uint32_t)i8_encode(kf[i] / a.k_scale) & 0xFFu;
-        vcode[i] = (uint32_t)i8_encode(vf[i] / a.v_scale) & 0xFFu;
+      } else if constexpr (KV == KV_I8) {
+        kcode[i] = (uint32_t)i8_encode(kf[i] / ks) & 0xFFu;
+        vcode[i] = (uint32_t)i8_encode(vf[i] / vs) & 0xFFu;
+      } else {            // a zero row (scale 0) codes to 0
+        kcode[i] = ks > 0.0f ? (uint32_t)i8_encode(kf[i] / ks) & 0xFFu : 0u;
+        vcode[i] = vs > 0.0f ? (uint32_t)i8_encode(vf[i] / vs) & 0xFFu : 0u;
       }
     }
 
@@ -130,7 +157,8 @@ __global__ void __launch_bounds__(256) kv_gather_kernel(GatherLaunch a) {
       } else {
         // decode through the same fp16 converters the attention kernels use
         const f16x4 h4 = codes4_to_f16x4<KV>((uint32_t)blk[off]);
-        val = __fmul_rn((float)h4[0], a.scale);
+        const float sc = KV == KV_I8T ? a.scales[((int64_t)page * a.hkv + h) * kPage + t] : a.scale;
+        val = __fmul_rn((float)h4[0], sc);
       }
       o[i] = val;
     }
@@ -178,6 +206,7 @@ hipError_t launch_kv_store(const StoreLaunch& a, hipStream_t s) {
   switch (a.kv) {
     case KV_F16: return store_dispatch_d<KV_F16>(a, s, g, b);
     case KV_E4M3: return store_dispatch_d<KV_E4M3>(a, s, g, b);
+    case KV_I8T: return store_dispatch_d<KV_I8T>(a, s, g, b);
     default: return store_dispatch_d<KV_I8>(a, s, g, b);
   }
 }
@@ -188,6 +217,7 @@ hipError_t launch_kv_gather(const GatherLaunch& a, hipStream_t s) {
   switch (a.kv) {
     case KV_F16: return gather_dispatch_d<KV_F16>(a, s, g, b);
     case KV_E4M3: return gather_dispatch_d<KV_E4M3>(a, s, g, b);
+    case KV_I8T: return gather_dispatch_d<KV_I8T>(a, s, g, b);
     default: return gather_dispatch_d<KV_I8>(a, s, g, b);
   }
 }

@@ -38,15 +38,18 @@ int kv_kind(int32_t kv) {
     case RA_KV_F16: return ra::KV_F16;
     case RA_KV_FP8_E4M3: return ra::KV_E4M3;
     case RA_KV_INT8: return ra::KV_I8;
+    case RA_KV_INT8_TOKEN: return ra::KV_I8T;
     default: return -1;
   }
 }
 
 const char* kv_name(int32_t kv) {
-  return kv == RA_KV_F16 ? "FP16" : kv == RA_KV_FP8_E4M3 ? "FP8 E4M3" : "INT8";
+  return kv == RA_KV_F16 ? "FP16" : kv == RA_KV_FP8_E4M3 ? "FP8 E4M3" : kv == RA_KV_INT8 ? "INT8" : "per-token INT8";
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool per_layer_scales(int32_t kv) { return kv == RA_KV_FP8_E4M3 || kv == RA_KV_INT8; }
 
 // Split plan of an attention call: partition slots per sequence and, in the
 // automatic mode, each kernel's fixed partition size.
@@ -86,7 +89,7 @@ int32_t check_attn(const ra_attn_args* a, Plan* plan) {
                 a->max_context_len, (long long)a->block_table_stride * RA_KV_PAGE_SIZE);
   if (!(std::isfinite(a->softmax_scale) && a->softmax_scale > 0.0f))
     return fail(RA_ERR_INVALID_ARG, "ra_paged_attn: softmax_scale must be finite and > 0");
-  if (a->kv_dtype != RA_KV_F16 && !(good_scale(a->k_scale) && good_scale(a->v_scale)))
+  if (per_layer_scales(a->kv_dtype) && !(good_scale(a->k_scale) && good_scale(a->v_scale)))
     return fail(RA_ERR_INVALID_ARG,
                 "ra_paged_attn: %s KV needs finite positive per-layer k_scale and v_scale (got %g, %g); "
                 "there is no fallback scale", kv_name(a->kv_dtype), (double)a->k_scale, (double)a->v_scale);
@@ -136,6 +139,12 @@ int32_t check_attn_pointers(const ra_attn_args* a, const Plan& p) {
                 "ra_paged_attn: q, k_cache, v_cache, block_tables, context_lens and query_start_loc must be non-NULL");
   if (!aligned16(a->q) || !aligned16(a->k_cache) || !aligned16(a->v_cache) || (a->out && !aligned16(a->out)))
     return fail(RA_ERR_MISALIGNED, "ra_paged_attn: q, out, k_cache and v_cache must be 16-byte aligned");
+  if (a->kv_dtype == RA_KV_INT8_TOKEN) {
+    if (!a->k_scales || !a->v_scales)
+      return fail(RA_ERR_INVALID_ARG, "ra_paged_attn: per-token INT8 KV needs the k_scales and v_scales planes");
+    if (!aligned16(a->k_scales) || !aligned16(a->v_scales))
+      return fail(RA_ERR_MISALIGNED, "ra_paged_attn: k_scales and v_scales must be 16-byte aligned");
+  }
   if (!p.direct) {
     if (!a->partial_out || !a->partial_lse)
       return fail(RA_ERR_WORKSPACE, "ra_paged_attn: %d partition slot(s) need partial_out and partial_lse%s",
@@ -160,9 +169,11 @@ ra::AttnLaunch make_launch(const ra_attn_args* a, const Plan& p) {
   L.k_cache = static_cast<const uint8_t*>(a->k_cache);
   L.v_cache = static_cast<const uint8_t*>(a->v_cache);
   L.kv = kv_kind(a->kv_dtype);
-  const bool quant = a->kv_dtype != RA_KV_F16;
+  const bool quant = per_layer_scales(a->kv_dtype);
   L.k_scale = quant ? a->k_scale : 1.0f;
   L.v_scale = quant ? a->v_scale : 1.0f;
+  L.k_scales = a->kv_dtype == RA_KV_INT8_TOKEN ? a->k_scales : nullptr;
+  L.v_scales = a->kv_dtype == RA_KV_INT8_TOKEN ? a->v_scales : nullptr;
   L.block_tables = a->block_tables;
   L.bt_stride = a->block_table_stride;
   L.context_lens = a->context_lens;
@@ -184,6 +195,49 @@ ra::AttnLaunch make_launch(const ra_attn_args* a, const Plan& p) {
   return L;
 }
 
+int32_t store_common(const char* fn, const void* k, const void* v, int32_t src_dtype, int64_t k_token_stride,
+                     int64_t v_token_stride, const int64_t* slot_mapping, int64_t num_tokens, void* k_cache,
+                     void* v_cache, int32_t kv_dtype, float* k_scales, float* v_scales, int64_t num_pages,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t page_size, float k_scale, float v_scale,
+                     void* stream) {
+  if (num_tokens < 0) return fail(RA_ERR_INVALID_ARG, "%s: num_tokens must be >= 0", fn);
+  if (src_dtype != RA_F16 && src_dtype != RA_BF16)
+    return fail(RA_ERR_UNSUPPORTED, "%s: src_dtype %d is not RA_F16 or RA_BF16", fn, src_dtype);
+  if (kv_kind(kv_dtype) < 0) return fail(RA_ERR_UNSUPPORTED, "%s: unknown kv_dtype %d", fn, kv_dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(RA_ERR_UNSUPPORTED, "%s: head_dim %d is not 64 or 128", fn, head_dim);
+  if (page_size != RA_KV_PAGE_SIZE) return fail(RA_ERR_UNSUPPORTED, "%s: page_size %d is not 16", fn, page_size);
+  if (num_kv_heads < 1) return fail(RA_ERR_INVALID_ARG, "%s: num_kv_heads must be >= 1", fn);
+  if (num_pages < 1) return fail(RA_ERR_INVALID_ARG, "%s: num_pages must be >= 1", fn);
+  if (per_layer_scales(kv_dtype) && !(good_scale(k_scale) && good_scale(v_scale)))
+    return fail(RA_ERR_INVALID_ARG,
+                "%s: %s KV needs finite positive per-layer k_scale and v_scale (got %g, %g); "
+                "there is no fallback scale", fn, kv_name(kv_dtype), (double)k_scale, (double)v_scale);
+  if (k_token_stride < (int64_t)num_kv_heads * head_dim || v_token_stride < (int64_t)num_kv_heads * head_dim)
+    return fail(RA_ERR_INVALID_ARG, "%s: token strides (%lld, %lld) smaller than num_kv_heads * head_dim", fn,
+                (long long)k_token_stride, (long long)v_token_stride);
+  if (num_tokens > (int64_t)(1 << 30) / ((int64_t)num_kv_heads * (head_dim / 8)))
+    return fail(RA_ERR_INVALID_ARG,
+                "%s: num_tokens * num_kv_heads * head_dim / 8 must not exceed 2^30; store in chunks", fn);
+  if (num_tokens == 0) return RA_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache)
+    return fail(RA_ERR_INVALID_ARG, "%s: k, v, slot_mapping, k_cache and v_cache must be non-NULL", fn);
+  if (kv_dtype == RA_KV_INT8_TOKEN && (!k_scales || !v_scales))
+    return fail(RA_ERR_INVALID_ARG, "%s: k_scales and v_scales must be non-NULL", fn);
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache) || (k_token_stride % 8) ||
+      (v_token_stride % 8) || (kv_dtype == RA_KV_INT8_TOKEN && (!aligned16(k_scales) || !aligned16(v_scales))))
+    return fail(RA_ERR_MISALIGNED,
+                "%s: k, v, k_cache, v_cache (and scale planes) must be 16-byte aligned and token strides "
+                "multiples of 8", fn);
+  const bool quant = per_layer_scales(kv_dtype);
+  ra::StoreLaunch L{k, v, src_dtype == RA_BF16, k_token_stride, v_token_stride, slot_mapping, num_tokens,
+                    k_cache, v_cache, kv_kind(kv_dtype), num_pages, num_kv_heads, head_dim,
+                    quant ? k_scale : 1.0f, quant ? v_scale : 1.0f, k_scales, v_scales};
+  const hipError_t e = ra::launch_kv_store(L, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(RA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return RA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -192,39 +246,20 @@ int32_t ra_kv_store(const void* k, const void* v, int32_t src_dtype, int64_t k_t
                     int64_t v_token_stride, const int64_t* slot_mapping, int64_t num_tokens, void* k_cache,
                     void* v_cache, int32_t kv_dtype, int64_t num_pages, int32_t num_kv_heads, int32_t head_dim,
                     int32_t page_size, float k_scale, float v_scale, void* stream) {
-  if (num_tokens < 0) return fail(RA_ERR_INVALID_ARG, "ra_kv_store: num_tokens must be >= 0");
-  if (src_dtype != RA_F16 && src_dtype != RA_BF16)
-    return fail(RA_ERR_UNSUPPORTED, "ra_kv_store: src_dtype %d is not RA_F16 or RA_BF16", src_dtype);
-  if (kv_kind(kv_dtype) < 0) return fail(RA_ERR_UNSUPPORTED, "ra_kv_store: unknown kv_dtype %d", kv_dtype);
-  if (head_dim != 64 && head_dim != 128)
-    return fail(RA_ERR_UNSUPPORTED, "ra_kv_store: head_dim %d is not 64 or 128", head_dim);
-  if (page_size != RA_KV_PAGE_SIZE)
-    return fail(RA_ERR_UNSUPPORTED, "ra_kv_store: page_size %d is not 16", page_size);
-  if (num_kv_heads < 1) return fail(RA_ERR_INVALID_ARG, "ra_kv_store: num_kv_heads must be >= 1");
-  if (num_pages < 1) return fail(RA_ERR_INVALID_ARG, "ra_kv_store: num_pages must be >= 1");
-  if (kv_dtype != RA_KV_F16 && !(good_scale(k_scale) && good_scale(v_scale)))
-    return fail(RA_ERR_INVALID_ARG,
-                "ra_kv_store: %s KV needs finite positive per-layer k_scale and v_scale (got %g, %g); "
-                "there is no fallback scale", kv_name(kv_dtype), (double)k_scale, (double)v_scale);
-  if (k_token_stride < (int64_t)num_kv_heads * head_dim || v_token_stride < (int64_t)num_kv_heads * head_dim)
-    return fail(RA_ERR_INVALID_ARG, "ra_kv_store: token strides (%lld, %lld) smaller than num_kv_heads * head_dim",
-                (long long)k_token_stride, (long long)v_token_stride);
-  if (num_tokens > (int64_t)(1 << 30) / ((int64_t)num_kv_heads * (head_dim / 8)))
-    return fail(RA_ERR_INVALID_ARG,
-                "ra_kv_store: num_tokens * num_kv_heads * head_dim / 8 must not exceed 2^30; store in chunks");
-  if (num_tokens == 0) return RA_OK;
-  if (!k || !v || !slot_mapping || !k_cache || !v_cache)
-    return fail(RA_ERR_INVALID_ARG, "ra_kv_store: k, v, slot_mapping, k_cache and v_cache must be non-NULL");
-  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache) || (k_token_stride % 8) ||
-      (v_token_stride % 8))
-    return fail(RA_ERR_MISALIGNED,
-                "ra_kv_store: k, v, k_cache, v_cache must be 16-byte aligned and token strides multiples of 8");
-  ra::StoreLaunch L{k, v, src_dtype == RA_BF16, k_token_stride, v_token_stride, slot_mapping, num_tokens,
-                    k_cache, v_cache, kv_kind(kv_dtype), num_pages, num_kv_heads, head_dim,
-                    kv_dtype == RA_KV_F16 ? 1.0f : k_scale, kv_dtype == RA_KV_F16 ? 1.0f : v_scale};
-  const hipError_t e = ra::launch_kv_store(L, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(RA_ERR_HIP, "ra_kv_store: launch failed: %s", hipGetErrorString(e));
-  return RA_OK;
+  if (kv_dtype == RA_KV_INT8_TOKEN)
+    return fail(RA_ERR_UNSUPPORTED, "ra_kv_store: per-token INT8 KV is stored with ra_kv_store_int8_token");
+  return store_common("ra_kv_store", k, v, src_dtype, k_token_stride, v_token_stride, slot_mapping, num_tokens,
+                      k_cache, v_cache, kv_dtype, nullptr, nullptr, num_pages, num_kv_heads, head_dim, page_size,
+                      k_scale, v_scale, stream);
+}
+
+int32_t ra_kv_store_int8_token(const void* k, const void* v, int32_t src_dtype, int64_t k_token_stride,
+                               int64_t v_token_stride, const int64_t* slot_mapping, int64_t num_tokens,
+                               void* k_cache, void* v_cache, float* k_scales, float* v_scales, int64_t num_pages,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t page_size, void* stream) {
+  return store_common("ra_kv_store_int8_token", k, v, src_dtype, k_token_stride, v_token_stride, slot_mapping,
+                      num_tokens, k_cache, v_cache, RA_KV_INT8_TOKEN, k_scales, v_scales, num_pages, num_kv_heads,
+                      head_dim, page_size, 1.0f, 1.0f, stream);
 }
 
 int32_t ra_paged_attn_workspace(const ra_attn_args* args, int32_t* slots, int64_t* partial_out_floats,
@@ -284,7 +319,7 @@ int32_t ra_lse_merge(const float* partial_out, const float* partial_lse, int32_t
   return RA_OK;
 }
 
-int32_t ra_kv_gather_dequant(const void* cache, int32_t which, int32_t kv_dtype, float scale,
+int32_t ra_kv_gather_dequant(const void* cache, int32_t which, int32_t kv_dtype, float scale, const float* scales,
                              const int32_t* block_table_row, int32_t ctx, int64_t num_pages, int32_t num_kv_heads,
                              int32_t head_dim, float* out, void* stream) {
   if (which != 0 && which != 1) return fail(RA_ERR_INVALID_ARG, "ra_kv_gather_dequant: which must be 0 (K) or 1 (V)");
@@ -293,14 +328,16 @@ int32_t ra_kv_gather_dequant(const void* cache, int32_t which, int32_t kv_dtype,
     return fail(RA_ERR_UNSUPPORTED, "ra_kv_gather_dequant: head_dim %d is not 64 or 128", head_dim);
   if (ctx < 0 || num_pages < 1 || num_kv_heads < 1)
     return fail(RA_ERR_INVALID_ARG, "ra_kv_gather_dequant: ctx >= 0, num_pages >= 1 and num_kv_heads >= 1 required");
-  if (kv_dtype != RA_KV_F16 && !good_scale(scale))
+  if (per_layer_scales(kv_dtype) && !good_scale(scale))
     return fail(RA_ERR_INVALID_ARG, "ra_kv_gather_dequant: scale must be finite and > 0");
   if (ctx == 0) return RA_OK;
   if (!cache || !block_table_row || !out)
     return fail(RA_ERR_INVALID_ARG, "ra_kv_gather_dequant: cache, block_table_row and out must be non-NULL");
   if (!aligned16(cache)) return fail(RA_ERR_MISALIGNED, "ra_kv_gather_dequant: cache must be 16-byte aligned");
-  ra::GatherLaunch G{cache, which, kv_kind(kv_dtype), kv_dtype == RA_KV_F16 ? 1.0f : scale, block_table_row, ctx,
-                     num_pages, num_kv_heads, head_dim, out};
+  if (kv_dtype == RA_KV_INT8_TOKEN && !scales)
+    return fail(RA_ERR_INVALID_ARG, "ra_kv_gather_dequant: per-token INT8 KV needs its scale plane");
+  ra::GatherLaunch G{cache, which, kv_kind(kv_dtype), per_layer_scales(kv_dtype) ? scale : 1.0f, block_table_row,
+                     ctx, num_pages, num_kv_heads, head_dim, out, scales};
   const hipError_t e = ra::launch_kv_gather(G, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(RA_ERR_HIP, "ra_kv_gather_dequant: launch failed: %s", hipGetErrorString(e));
   return RA_OK;

@@ -8,7 +8,8 @@
 
 namespace ra {
 
-enum KvKind { KV_F16 = 0, KV_E4M3 = 1, KV_I8 = 2 };
+// KV_I8T: INT8 codes with fp32 scales per (token, head) in separate planes.
+enum KvKind { KV_F16 = 0, KV_E4M3 = 1, KV_I8 = 2, KV_I8T = 3 };
 
 struct StoreLaunch {
   const void* k;
@@ -26,6 +27,8 @@ struct StoreLaunch {
   int head_dim;
   float k_scale;
   float v_scale;
+  float* k_scales;       // KV_I8T scale planes [num_pages][hkv][16]
+  float* v_scales;
 };
 hipError_t launch_kv_store(const StoreLaunch& a, hipStream_t s);
 
@@ -40,6 +43,7 @@ struct GatherLaunch {
   int hkv;
   int head_dim;
   float* out;
+  const float* scales;   // KV_I8T scale plane
 };
 hipError_t launch_kv_gather(const GatherLaunch& a, hipStream_t s);
 
@@ -76,6 +80,8 @@ struct AttnLaunch {
   int32_t part_tokens;   // auto mode: partition size (tokens) of units with >= kSmallUnitRows rows
   int32_t part_small;    // auto mode: partition size of units with fewer rows
   bool direct;           // write out/lse directly (one slot)
+  const float* k_scales; // KV_I8T scale planes [num_pages][hkv][16]
+  const float* v_scales;
 };
 
 // Rows of a (sequence, KV head) unit: g * q_len, in 16-row matrix-core tiles

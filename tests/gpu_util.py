@@ -38,6 +38,10 @@ class DeviceWorkload:
         D, hkv = w.head_dim, w.num_kv_heads
         self.k_cache = P.new_cache(w.num_pages, hkv, D, w.kv_dtype, device, fill=w.cache_sentinel)
         self.v_cache = P.new_cache(w.num_pages, hkv, D, w.kv_dtype, device, fill=w.cache_sentinel)
+        self.k_scales = self.v_scales = None
+        if w.kv_dtype == "int8_tok":          # unwritten scales read as NaN
+            self.k_scales = P.new_scale_plane(w.num_pages, hkv, device)
+            self.v_scales = P.new_scale_plane(w.num_pages, hkv, device)
         if store:
             U = w.tokens_k.shape[0]
             for lo in range(0, U, chunk_tokens):
@@ -45,7 +49,8 @@ class DeviceWorkload:
                 k = t_src(w.tokens_k[lo:hi], w.src_dtype, device)
                 v = t_src(w.tokens_v[lo:hi], w.src_dtype, device)
                 s = torch.from_numpy(w.token_slots[lo:hi]).to(device)
-                P.kv_store(k, v, s, self.k_cache, self.v_cache, w.kv_dtype, w.k_scale, w.v_scale)
+                P.kv_store(k, v, s, self.k_cache, self.v_cache, w.kv_dtype, w.k_scale, w.v_scale,
+                           k_scales=self.k_scales, v_scales=self.v_scales)
         self.q = t_src(w.q, w.q_dtype, device)
         self.block_tables = torch.from_numpy(w.block_tables).to(device)
         self.context_lens = torch.from_numpy(w.ctx).to(device)
@@ -60,7 +65,7 @@ class DeviceWorkload:
                             min_q_len=int(w.q_len.min()), max_context_len=w.max_context_len,
                             window_left=w.window_left, num_sinks=w.num_sinks,
                             num_splits=w.num_splits if num_splits is None else num_splits,
-                            partials_only=partials_only, **kw)
+                            partials_only=partials_only, k_scales=self.k_scales, v_scales=self.v_scales, **kw)
 
 
 def dequant_tokens(w, rows, which, heads=None):
@@ -69,7 +74,7 @@ def dequant_tokens(w, rows, which, heads=None):
     scale = w.k_scale if which == "k" else w.v_scale
     x = src[rows] if heads is None else src[rows][:, heads]
     x32 = OC.source_to_f32(x, w.src_dtype)
-    return OC.dequantize(OC.quantize(x32, w.kv_dtype, scale), w.kv_dtype, scale)
+    return OC.roundtrip(x32, w.kv_dtype, scale)
 
 
 def q_f64(w, b):

@@ -47,7 +47,7 @@ def test_exports_every_declared_symbol():
 
 def test_abi_version():
     L = _lib()
-    assert L.abi_version() == 1001
+    assert L.abi_version() == 2001
 
 
 def test_struct_layout_matches_c():
@@ -244,16 +244,67 @@ def test_merge_validation(args, status, msg):
 
 
 @pytest.mark.parametrize("args,status,msg", [
-    ((FAKE, 2, 2, 0.1, FAKE, 16, 4, 1, 128, FAKE), 1, "which"),
-    ((FAKE, 0, 5, 0.1, FAKE, 16, 4, 1, 128, FAKE), 2, "kv_dtype"),
-    ((FAKE, 0, 2, 0.1, FAKE, 16, 4, 1, 48, FAKE), 2, "head_dim"),
-    ((FAKE, 0, 2, 0.0, FAKE, 16, 4, 1, 128, FAKE), 1, "scale"),
-    ((FAKE, 0, 2, 0.1, FAKE, -1, 4, 1, 128, FAKE), 1, "ctx"),
-    ((0, 0, 2, 0.1, FAKE, 16, 4, 1, 128, FAKE), 1, "non-NULL"),
-    ((FAKE + 2, 0, 2, 0.1, FAKE, 16, 4, 1, 128, FAKE), 3, "aligned"),
+    ((FAKE, 2, 2, 0.1, None, FAKE, 16, 4, 1, 128, FAKE), 1, "which"),
+    ((FAKE, 0, 5, 0.1, None, FAKE, 16, 4, 1, 128, FAKE), 2, "kv_dtype"),
+    ((FAKE, 0, 2, 0.1, None, FAKE, 16, 4, 1, 48, FAKE), 2, "head_dim"),
+    ((FAKE, 0, 2, 0.0, None, FAKE, 16, 4, 1, 128, FAKE), 1, "scale"),
+    ((FAKE, 0, 2, 0.1, None, FAKE, -1, 4, 1, 128, FAKE), 1, "ctx"),
+    ((0, 0, 2, 0.1, None, FAKE, 16, 4, 1, 128, FAKE), 1, "non-NULL"),
+    ((FAKE + 2, 0, 2, 0.1, None, FAKE, 16, 4, 1, 128, FAKE), 3, "aligned"),
+    ((FAKE, 0, 4, 0.0, None, FAKE, 16, 4, 1, 128, FAKE), 1, "scale plane"),
 ])
 def test_gather_validation(args, status, msg):
     L = _lib()
     lib = L.load_library()
     st = lib.ra_kv_gather_dequant(*args, None)
     assert st == status and msg in lib.ra_last_error().decode()
+
+
+def _store_tok(lib, **kw):
+    args = dict(k=FAKE, v=FAKE, src=1, ks=256, vs=256, slots=FAKE, n=4, kc=FAKE, vc=FAKE, kp=FAKE, vp=FAKE,
+                pages=10, hkv=2, d=128, page=16)
+    args.update(kw)
+    return lib.ra_kv_store_int8_token(args["k"], args["v"], args["src"], args["ks"], args["vs"], args["slots"],
+                                      args["n"], args["kc"], args["vc"], args["kp"], args["vp"], args["pages"],
+                                      args["hkv"], args["d"], args["page"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(kp=0), 1, "k_scales and v_scales"),
+    (dict(vp=0), 1, "k_scales and v_scales"),
+    (dict(kp=FAKE + 4), 3, "aligned"),
+    (dict(d=96), 2, "head_dim"),
+    (dict(n=-2), 1, "num_tokens"),
+])
+def test_store_int8_token_validation(kw, status, msg):
+    L = _lib()
+    lib = L.load_library()
+    st = _store_tok(lib, **kw)
+    assert st == status, (st, lib.ra_last_error())
+    assert msg in lib.ra_last_error().decode()
+    assert _store_tok(lib, n=0, kp=0) == 0
+
+
+def test_plain_store_refuses_per_token_format():
+    L = _lib()
+    lib = L.load_library()
+    assert _store(lib, kv=4) == 2
+    assert "ra_kv_store_int8_token" in lib.ra_last_error().decode()
+
+
+def test_attn_int8_token_needs_aligned_planes_and_ignores_layer_scales():
+    L = _lib()
+    lib = L.load_library()
+    a = _good_args(L, kv_dtype=L.RA_KV_INT8_TOKEN, k_scale=0.0, v_scale=float("nan"))
+    a.k_scales = None
+    a.v_scales = FAKE
+    assert lib.ra_paged_attn(ctypes.byref(a), None) == 1
+    assert "k_scales and v_scales" in lib.ra_last_error().decode()
+    a.k_scales = FAKE + 8
+    assert lib.ra_paged_attn(ctypes.byref(a), None) == 3
+    # the per-layer scales are not checked for this format: only the planes are
+    slots = ctypes.c_int32()
+    po = ctypes.c_int64()
+    pl = ctypes.c_int64()
+    a.k_scales = FAKE
+    assert lib.ra_paged_attn_workspace(ctypes.byref(a), ctypes.byref(slots), ctypes.byref(po), ctypes.byref(pl)) == 0

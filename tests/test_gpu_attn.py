@@ -40,6 +40,10 @@ CASES = [
     # decode auto partitions around their rule's bends: 512 tokens up to 16K,
     # ~32 partitions up to 64K, 2048 tokens beyond
     ("dec_g8_e4m3_auto_bends", [16384, 16400, 65536, 65552, 100000, 511], 1, 16, 2, 128, "e4m3", "f16", -1, 0, 0),
+    # INT8 with runtime scales per token and head
+    ("mfma_g8_q5_int8tok", [1000, 77, 513, 40], 5, 16, 2, 128, "int8_tok", "f16", -1, 0, 3),
+    ("dec_g8_int8tok_auto", [3000, 77, 513], 1, 16, 2, 128, "int8_tok", "bf16", -1, 0, 0),
+    ("mfma_g8_q16_int8tok_window_d64", [900, 300], 16, 16, 2, 64, "int8_tok", "f16", 100, 4, 2),
 ]
 
 
@@ -136,7 +140,7 @@ def _single(w, b):
     return q0, q1
 
 
-@pytest.mark.parametrize("case", [CASES[1], CASES[8], CASES[14], CASES[17], CASES[22]], ids=lambda c: c[0])
+@pytest.mark.parametrize("case", [CASES[1], CASES[8], CASES[14], CASES[17], CASES[22], CASES[24]], ids=lambda c: c[0])
 def test_batch_invariance_bitwise(case):
     """A sequence's result does not depend on the rest of the batch (other
     lengths change the automatic split count, and mixing decode with verify
@@ -153,7 +157,8 @@ def test_batch_invariance_bitwise(case):
                               kv_dtype=w.kv_dtype, k_scale=w.k_scale, v_scale=w.v_scale,
                               softmax_scale=w.softmax_scale, max_q_len=ql, min_q_len=ql,
                               max_context_len=int(w.ctx[b]), window_left=w.window_left,
-                              num_sinks=w.num_sinks, num_splits=w.num_splits)
+                              num_sinks=w.num_sinks, num_splits=w.num_splits,
+                              k_scales=dw.k_scales, v_scales=dw.v_scales)
         torch.cuda.synchronize()
         assert torch.equal(o1.view(torch.int16), out[q0:q1].view(torch.int16)), (case[0], b)
         assert torch.equal(l1.view(torch.int32), lse[q0:q1].view(torch.int32)), (case[0], b)

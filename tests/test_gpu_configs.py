@@ -1,4 +1,4 @@
-"""GPU parity on the five benchmark workloads at full size, in the launch
+"""GPU parity on the benchmark workloads at full size, in the launch
 configuration bench.py times.
 
 Store: bit-exact on a random sample of tokens (their bytes in the GPU caches
@@ -25,6 +25,9 @@ CONFIGS = [
     ("verify_fp8_32k", W.verify_fp8_32k, [(0, 0), (5, 1), (7, 1)]),
     ("prefix_int8_256k", W.prefix_int8_256k, [(0, 1), (3, 0)]),
     ("split_fp8_512k", W.split_fp8_512k, [(1, 0)]),
+    # beyond the five: plain decode at 32K, and per-token INT8 at the verify shape
+    ("decode_fp8_32k", W.decode_fp8_32k, [(2, 1)]),
+    ("verify_int8tok_32k", W.verify_int8tok_32k, [(0, 1), (6, 0)]),
 ]
 
 
@@ -39,7 +42,13 @@ def _check_store_sample(w, dw, n=48, seed=0):
         local = np.searchsorted(pages, slots // 16) * 16 + slots % 16
         got = OL.gather(sel, local, which, w.num_kv_heads, w.head_dim, w.kv_dtype)
         src = w.tokens_k[rows] if which == "k" else w.tokens_v[rows]
-        want = OC.quantize(OC.source_to_f32(src, w.src_dtype), w.kv_dtype, scale)
+        if w.kv_dtype == "int8_tok":
+            want, want_sc = OC.quantize_per_token(OC.source_to_f32(src, w.src_dtype))
+            plane = (dw.k_scales if which == "k" else dw.v_scales).cpu().numpy().reshape(-1)
+            got_sc = OL.gather_scales(plane, slots, w.num_kv_heads)
+            assert np.array_equal(got_sc.view(np.uint32), want_sc.view(np.uint32)), f"{w.name} {which} scales differ"
+        else:
+            want = OC.quantize(OC.source_to_f32(src, w.src_dtype), w.kv_dtype, scale)
         assert np.array_equal(np.ascontiguousarray(got).view(np.uint8),
                               np.ascontiguousarray(want).view(np.uint8)), f"{w.name} {which} store differs"
     used = set(np.unique(w.token_slots // 16).tolist())

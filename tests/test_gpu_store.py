@@ -162,3 +162,45 @@ def test_gather_dequant_f16_and_bad_page():
     assert np.isnan(got[16:32]).all()
     assert np.array_equal(got[32:], want[32:])
     log("gather ok")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("src", ["f16", "bf16"])
+def test_store_int8_token_codes_and_scales_bit_exact(D, src):
+    """Per-token INT8: the codes in the cache and the fp32 scales in the two
+    planes equal the oracle's, bit for bit; unwritten scales stay NaN."""
+    w = W.build(f"store_int8tok_{D}_{src}", 12, ctx=[50, 33, 70, 16, 1], q_len=1, num_q_heads=4, num_kv_heads=2,
+                head_dim=D, kv_dtype="int8_tok", src_dtype=src, q_dtype="f16", pool_pages=24)
+    rng = np.random.default_rng(3)
+    # a zero row and rows of very different magnitude
+    w.tokens_k[5, 1] = 0
+    w.tokens_v[7, 0] = 0
+    if src == "f16":
+        w.tokens_k[9] = (w.tokens_k[9].astype(np.float32) * 300).astype(np.float16)
+        w.tokens_v[11] = (w.tokens_v[11].astype(np.float32) * 1e-3).astype(np.float16)
+    dw = DeviceWorkload(w)
+    torch.cuda.synchronize()
+    e = 1
+    nbytes = w.num_pages * w.num_kv_heads * 16 * w.head_dim * e
+    for which, cache, plane in (("k", dw.k_cache, dw.k_scales), ("v", dw.v_cache, dw.v_scales)):
+        src_x = w.tokens_k if which == "k" else w.tokens_v
+        codes, sc = OC.quantize_per_token(OC.source_to_f32(src_x, w.src_dtype))
+        want = OL.scatter(np.full(nbytes, w.cache_sentinel, np.uint8), codes, w.token_slots, which,
+                          w.num_kv_heads, w.head_dim, "int8_tok")
+        got = _gpu_bytes(cache)
+        diff = np.nonzero(got != want)[0]
+        assert diff.size == 0, f"{which}: {diff.size} code bytes differ, first at {diff[:8]}"
+        want_plane = OL.scatter_scales(np.full(w.num_pages * w.num_kv_heads * 16, np.nan, np.float32), sc,
+                                       w.token_slots, w.num_kv_heads)
+        got_plane = plane.cpu().numpy().reshape(-1)
+        assert np.array_equal(got_plane.view(np.uint32), want_plane.view(np.uint32)), f"{which}: scales differ"
+    # exact read-back through a block table, scale plane included
+    for b in range(w.batch):
+        bt = torch.from_numpy(w.block_tables[b]).cuda()
+        ctx = int(w.ctx[b])
+        rows = w.seq_rows[b]
+        for which, cache, plane in ((0, dw.k_cache, dw.k_scales), (1, dw.v_cache, dw.v_scales)):
+            got = P.kv_gather_dequant(cache, which, "int8_tok", 1.0, bt, ctx, w.head_dim, scales=plane)
+            src_x = w.tokens_k if which == 0 else w.tokens_v
+            want = OC.roundtrip(OC.source_to_f32(src_x[rows], w.src_dtype), "int8_tok")
+            assert np.array_equal(got.cpu().numpy().view(np.uint32), want.view(np.uint32)), (b, which)
