@@ -159,6 +159,16 @@ int32_t ra_kv_store_int8_token(const void* k, const void* v, int32_t src_dtype,
  * lse = natural log of the softmax denominator (max-shifted form); a row with
  * no visible key gets out = 0, lse = -inf.
  *
+ * Context parallelism (ReVolta README, "Quick start", DCP2): a GPU may hold
+ * only a range of each sequence's keys.  Then kv_pos0[b] gives the global
+ * position of the cache's key 0 and q_pos0[b] the global position of the
+ * block's first query (query i at q_pos0[b] + i); ctx_b counts the keys this
+ * cache holds (q_len_b <= ctx_b is then not required, and a GPU holding
+ * none of a sequence's keys passes ctx_b = 0).  Visibility, windows and sinks
+ * use global positions.  Each GPU's (out, lse), with out = NULL its partials,
+ * combine across GPUs with ra_lse_merge.  NULL arrays mean kv_pos0 = 0 and
+ * q_pos0 = ctx_b - q_len_b.
+ *
  * Splitting: the keys of sequence b are cut into partitions of P_b tokens;
  * num_splits = S > 0 gives P_b = 16 * ceil(ceil(ctx_b / S) / 16) (S slots per
  * sequence); num_splits = 0 uses a fixed partition size chosen by the library
@@ -203,6 +213,8 @@ typedef struct ra_attn_args {
   int32_t partial_slots;           /* slots the partial buffers hold             */
   const float* k_scales;           /* RA_KV_INT8_TOKEN: scale planes (layout     */
   const float* v_scales;           /* above); ignored by the other formats       */
+  const int32_t* kv_pos0;          /* [batch] or NULL: global position of key 0  */
+  const int32_t* q_pos0;           /* [batch] or NULL: global position of query 0*/
 } ra_attn_args;
 
 /*

@@ -64,6 +64,8 @@ class AttnArgs(_c.Structure):
         ("partial_slots", _c.c_int32),
         ("k_scales", _vp),
         ("v_scales", _vp),
+        ("kv_pos0", _vp),
+        ("q_pos0", _vp),
     ]
 
 
@@ -177,7 +179,7 @@ def kv_store(k, v, slot_mapping, k_cache, v_cache, kv_dtype, k_scale=1.0, v_scal
 
 def _attn_args(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, kv_dtype, k_scale,
                v_scale, softmax_scale, max_q_len, min_q_len, max_context_len, window_left, num_sinks,
-               num_splits, num_kv_heads, k_scales=None, v_scales=None):
+               num_splits, num_kv_heads, k_scales=None, v_scales=None, kv_pos0=None, q_pos0=None):
     T, hq, D = q.shape
     a = AttnArgs()
     a.struct_size = _c.sizeof(AttnArgs)
@@ -208,6 +210,8 @@ def _attn_args(q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
     a.num_splits = int(num_splits)
     a.k_scales = None if k_scales is None else k_scales.data_ptr()
     a.v_scales = None if v_scales is None else v_scales.data_ptr()
+    a.kv_pos0 = None if kv_pos0 is None else kv_pos0.data_ptr()
+    a.q_pos0 = None if q_pos0 is None else q_pos0.data_ptr()
     return a
 
 
@@ -222,7 +226,7 @@ def paged_attn_workspace(args):
 def paged_attn(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, *, kv_dtype,
                max_q_len, max_context_len, k_scale=1.0, v_scale=1.0, softmax_scale=None, min_q_len=0,
                window_left=-1, num_sinks=0, num_splits=0, out=None, lse=None, partials_only=False,
-               workspace=None, stream=None, k_scales=None, v_scales=None):
+               workspace=None, stream=None, k_scales=None, v_scales=None, kv_pos0=None, q_pos0=None):
     """Attention of the query blocks over the paged caches.
 
     q [total_q][Hq][D] fp16/bf16; block_tables int32 [B][stride];
@@ -234,7 +238,7 @@ def paged_attn(q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
     hkv = k_cache.shape[1]
     a = _attn_args(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, kv_dtype, k_scale,
                    v_scale, softmax_scale, max_q_len, min_q_len, max_context_len, window_left, num_sinks,
-                   num_splits, hkv, k_scales, v_scales)
+                   num_splits, hkv, k_scales, v_scales, kv_pos0, q_pos0)
     if not partials_only:
         if out is None:
             out = torch.empty_like(q)

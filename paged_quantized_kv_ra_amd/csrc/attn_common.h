@@ -1,14 +1,23 @@
-// attn_common.h -- work decomposition shared by the two attention kernels.
+// attn_common.h -- work decomposition of the attention kernel.
 //
 // One workgroup handles one (sequence b, KV head h, partition slot s, row group)
 // unit.  Rows of a unit are the query-block rows r = i * g + j (query token i of
 // the block, query head h * g + j), g = Hq / Hkv (ReVolta README, "Quick start":
 // MTP4 verifies 1 + 4 tokens per sequence; the graded shapes use grouped query
-// heads).  Partition s covers keys [s * P_b, min((s + 1) * P_b, ctx_b)); only
-// the pages holding a key visible to some row of the block are visited: the
-// sink pages [0, num_sinks) and the window pages [ctx - q_len - W + 1, ctx)
-// when a window is set (ReVolta README, "DFlash2 speculative decoding"; "ReVolta
-// 0.1.3", "Behaviour changes"), every page of the partition otherwise.
+// heads).  Partition s covers the sequence's keys [s * P_b, min((s + 1) * P_b,
+// ctx_b)); only the pages holding a key visible to some row of the block are
+// visited: keys up to the last query's position, restricted with a window to
+// the sink keys and to keys within W of the first query (ReVolta README,
+// "DFlash2 speculative decoding"; "ReVolta 0.1.3", "Behaviour changes").
+//
+// Positions.  The cache holds the sequence's keys 0 .. ctx_b - 1.  With
+// context parallelism (ReVolta README, "Quick start", DCP2) a GPU holds only a
+// range of a sequence's keys, starting at global position kv_pos0[b], and the
+// block's queries sit at global positions q_pos0[b] + i.  All masks work in
+// the cache's local key index: a query's local position is its global one
+// minus kv_pos0[b], and a sink bound num_sinks becomes num_sinks - kv_pos0[b].
+// Without the two arrays kv_pos0 = 0 and the queries are the last q_len
+// positions of the context, q_pos0 = ctx_b - q_len.
 #pragma once
 
 #include "ra_device.h"
@@ -36,19 +45,26 @@ __device__ __forceinline__ int32_t partition_tokens(const AttnLaunch& a, int32_t
   return min(max(p, a.part_small), a.part_tokens);
 }
 
-// Visible page ranges of partition [lo, hi) for a block of q_len queries.
-__device__ __forceinline__ UnitPages unit_pages(const AttnLaunch& a, int32_t ctx, int32_t q_len,
-                                                int32_t lo, int32_t hi) {
+// A unit's queries in the cache's local key index: query i of the block sits
+// at local position pmin + i (pmax for the last one); keys below `sinks` are
+// sink keys.
+struct SeqFrame {
+  int32_t pmin, pmax, sinks;
+};
+
+// Visible page ranges of partition [lo, hi).
+__device__ __forceinline__ UnitPages unit_pages(const AttnLaunch& a, const SeqFrame& f, int32_t lo, int32_t hi) {
   UnitPages u{0, 0, 0, 0};
+  hi = min(hi, f.pmax + 1);       // keys after the last query are seen by none
   if (lo >= hi) return u;
   if (a.window < 0) {
     u.p0a = lo / kPage;
     u.na = (hi + kPage - 1) / kPage - u.p0a;
     return u;
   }
-  // keys any query sees: [0, sinks) U [ctx - q_len - W + 1, ctx)
-  const int32_t wlo = max(ctx - q_len - a.window + 1, 0);
-  const int32_t sa0 = lo, sa1 = min(hi, a.sinks);
+  // keys any query sees: [0, sinks) U [pmin - W + 1, pmax]
+  const int32_t wlo = max(f.pmin - a.window + 1, 0);
+  const int32_t sa0 = lo, sa1 = min(hi, f.sinks);
   const int32_t sb0 = max(lo, wlo), sb1 = hi;
   int32_t pa0 = 0, pa1 = 0, pb0 = 0, pb1 = 0;
   if (sa1 > sa0) { pa0 = sa0 / kPage; pa1 = (sa1 + kPage - 1) / kPage; }
@@ -64,9 +80,9 @@ __device__ __forceinline__ UnitPages unit_pages(const AttnLaunch& a, int32_t ctx
   return u;
 }
 
-// Key j visible to the query at position pos.
-__device__ __forceinline__ bool key_visible(const AttnLaunch& a, int32_t j, int32_t pos) {
-  return j <= pos && (a.window < 0 || pos - j < a.window || j < a.sinks);
+// Key j visible to the query at (local) position pos.
+__device__ __forceinline__ bool key_visible(const AttnLaunch& a, const SeqFrame& f, int32_t j, int32_t pos) {
+  return j <= pos && (a.window < 0 || pos - j < a.window || j < f.sinks);
 }
 
 // Block index -> logical unit id.  Consecutive workgroups are dispatched to the
@@ -100,10 +116,22 @@ inline unsigned padded_grid(int64_t units) {
 }
 
 // Sequence preconditions that the host cannot check.  A violating sequence
-// gets NaN rows instead of an out-of-bounds access.
-__device__ __forceinline__ bool seq_ok(const AttnLaunch& a, int32_t ctx, int32_t q0, int32_t q1) {
-  return ctx >= 0 && ctx <= a.max_ctx && q0 >= 0 && q1 >= q0 && q1 <= a.total_q &&
-         q1 - q0 <= a.max_q_len && q1 - q0 <= ctx;
+// gets NaN rows instead of an out-of-bounds access.  Without explicit
+// positions the block's queries must be the context's last q_len tokens.
+__device__ __forceinline__ bool seq_ok(const AttnLaunch& a, int32_t ctx, int32_t q0, int32_t q1, int32_t kv0,
+                                       int32_t qp0) {
+  return ctx >= 0 && ctx <= a.max_ctx && q0 >= 0 && q1 >= q0 && q1 <= a.total_q && q1 - q0 <= a.max_q_len &&
+         (a.q_pos0 ? qp0 >= 0 : q1 - q0 <= ctx) && kv0 >= 0;
+}
+
+// The unit's frame (see "Positions" above).
+__device__ __forceinline__ SeqFrame seq_frame(const AttnLaunch& a, int32_t ctx, int32_t q_len, int32_t kv0,
+                                              int32_t qp0) {
+  SeqFrame f;
+  f.pmin = (a.q_pos0 ? qp0 : ctx - q_len + kv0) - kv0;
+  f.pmax = f.pmin + q_len - 1;
+  f.sinks = a.window < 0 ? 0 : a.sinks - kv0;
+  return f;
 }
 
 }  // namespace ra

@@ -206,7 +206,7 @@ template <int KV, int D, int NT>
 __device__ __forceinline__ void compute_page(Acc<KV, D, NT>& acc, PageRegs<KV, D>& r,
                                              const f16x8 (&qf)[NT][Geo<KV, D>::KS],
                                              const AttnLaunch& a, const UnitPages& pg, int32_t n, int32_t ctx,
-                                             int32_t q_len, const int32_t (&pos)[NT], int kgrp, float c,
+                                             const SeqFrame& fr, const int32_t (&pos)[NT], int kgrp, float c,
                                              float thr) {
   using G = Geo<KV, D>;
   // ---- scores S^T for the page's 16 keys
@@ -228,16 +228,17 @@ __device__ __forceinline__ void compute_page(Acc<KV, D, NT>& acc, PageRegs<KV, D
   // (stale bytes of the last page) also get their V codes zeroed so that
   // 0 * garbage cannot produce NaN.
   const int32_t tok0 = pg.page(n) * kPage;
-  const bool need_mask = (tok0 + kPage - 1 > ctx - q_len) || (a.window >= 0 && tok0 <= ctx - 1 - a.window);
+  const bool need_mask = (tok0 + kPage - 1 > fr.pmin) || (tok0 + kPage - 1 >= ctx) ||
+                         (a.window >= 0 && tok0 <= fr.pmax - a.window);
   if (need_mask) {
     const int32_t tb = tok0 + 4 * kgrp;
     uint32_t keep8 = 0, keep_lo = 0, keep_hi = 0;   // byte / half masks of the lane's 4 tokens
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int32_t j = tb + i;
+      const bool data = j < ctx;   // keys past ctx are stale bytes, whatever the query positions
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) s[nt][i] = key_visible(a, j, pos[nt]) ? s[nt][i] : -INFINITY;
-      const bool data = j < ctx;
+      for (int nt = 0; nt < NT; ++nt) s[nt][i] = data && key_visible(a, fr, j, pos[nt]) ? s[nt][i] : -INFINITY;
       if constexpr (KV == KV_I8T) r.vs[i] = data ? r.vs[i] : 0.0f;   // the scale plane past ctx is not data
       keep8 |= data ? 0xFFu << (8 * i) : 0u;
       if (i < 2) keep_lo |= data ? 0xFFFFu << (16 * i) : 0u;
@@ -326,7 +327,10 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a,
   const int32_t row0 = u.rg * kMfmaRowsPerBlock;
   if (row0 >= rows) return;
   const int32_t ctx = a.context_lens[u.b];
-  bool bad = !seq_ok(a, ctx, q0, q1);
+  const int32_t kv0 = a.kv_pos0 ? a.kv_pos0[u.b] : 0;
+  const int32_t qp0 = a.q_pos0 ? a.q_pos0[u.b] : 0;
+  bool bad = !seq_ok(a, ctx, q0, q1, kv0, qp0);
+  const SeqFrame fr = seq_frame(a, ctx, q_len, kv0, qp0);
 
   // partition and visible pages
   int32_t lo = 0, hi = 0;
@@ -335,7 +339,7 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a,
     const int32_t P = partition_tokens(a, ctx, rows);
     lo = u.s * P;
     hi = min(lo + P, ctx);
-    pg = unit_pages(a, ctx, q_len, lo, hi);
+    pg = unit_pages(a, fr, lo, hi);
   }
   const int32_t npages = pg.count();
   const int32_t* bt_row = a.block_tables + (int64_t)u.b * a.bt_stride;
@@ -365,7 +369,7 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a,
   for (int nt = 0; nt < NT; ++nt) {
     const int32_t r = row0 + nt * 16 + ncol;
     qlive[nt] = r < rows && !bad;
-    pos[nt] = qlive[nt] ? ctx - q_len + r / g : ctx - 1;
+    pos[nt] = fr.pmin + (qlive[nt] ? r / g : 0);
     const int64_t qrow = qlive[nt] ? ((int64_t)(q0 + r / g) * a.hq + u.h * g + r % g) : 0;
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + qrow * D + kgrp * (D / 4);
 #pragma unroll
@@ -428,7 +432,7 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a,
             wait_vmcnt<0>();
           PageRegs<KV, D> r;
           read_page<KV, D>(r, ring + j * G::NSL, scl + j * 32, lane_off, kgrp);
-          compute_page<KV, D, NT>(acc, r, qf, a, pg, ws.page(k), ctx, q_len, pos, kgrp, c, thr);
+          compute_page<KV, D, NT>(acc, r, qf, a, pg, ws.page(k), ctx, fr, pos, kgrp, c, thr);
           // the slot's reads have returned (their values were consumed) before
           // the next load may overwrite it
           wait_lgkmcnt0();

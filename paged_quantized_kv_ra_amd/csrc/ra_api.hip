@@ -174,6 +174,8 @@ ra::AttnLaunch make_launch(const ra_attn_args* a, const Plan& p) {
   L.v_scale = quant ? a->v_scale : 1.0f;
   L.k_scales = a->kv_dtype == RA_KV_INT8_TOKEN ? a->k_scales : nullptr;
   L.v_scales = a->kv_dtype == RA_KV_INT8_TOKEN ? a->v_scales : nullptr;
+  L.kv_pos0 = a->kv_pos0;
+  L.q_pos0 = a->q_pos0;
   L.block_tables = a->block_tables;
   L.bt_stride = a->block_table_stride;
   L.context_lens = a->context_lens;

@@ -82,6 +82,8 @@ struct AttnLaunch {
   bool direct;           // write out/lse directly (one slot)
   const float* k_scales; // KV_I8T scale planes [num_pages][hkv][16]
   const float* v_scales;
+  const int32_t* kv_pos0;  // [batch] global position of cache key 0, or nullptr (0)
+  const int32_t* q_pos0;   // [batch] global position of the block's first query, or nullptr
 };
 
 // Rows of a (sequence, KV head) unit: g * q_len, in 16-row matrix-core tiles
