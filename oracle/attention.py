@@ -49,12 +49,17 @@ import numpy as np
 PAGE = 16
 
 
-def visible_mask(ctx, q_len, window_left=-1, num_sinks=0, key_lo=0, key_hi=None):
-    """bool[q_len, ctx]: key j visible to query i (optionally inside [lo, hi))."""
+def visible_mask(ctx, q_len, window_left=-1, num_sinks=0, key_lo=0, key_hi=None, positions=None):
+    """bool[q_len, ctx]: key j visible to query i (optionally inside [lo, hi)).
+
+    Query i sits at position ``positions[i]``, by default ctx - q_len + i (the
+    block is the context's last q_len tokens)."""
     if key_hi is None:
         key_hi = ctx
     j = np.arange(ctx, dtype=np.int64)[None, :]
-    pos = (ctx - q_len + np.arange(q_len, dtype=np.int64))[:, None]
+    if positions is None:
+        positions = ctx - q_len + np.arange(q_len, dtype=np.int64)
+    pos = np.asarray(positions, dtype=np.int64)[:, None]
     vis = j <= pos
     if window_left is not None and window_left >= 0:
         vis &= ((pos - j) < window_left) | (j < num_sinks)
@@ -63,18 +68,21 @@ def visible_mask(ctx, q_len, window_left=-1, num_sinks=0, key_lo=0, key_hi=None)
 
 
 def attention(q, k, v, softmax_scale, window_left=-1, num_sinks=0,
-              key_lo=0, key_hi=None):
+              key_lo=0, key_hi=None, positions=None):
     """Attention of one sequence's query block.
 
     q: [q_len, Hq, D]; k, v: [ctx, Hkv, D] (dequantised values, any float
-    type).  Returns (out [q_len, Hq, D] float64, lse [q_len, Hq] float64).
+    type).  ``positions``: the queries' positions (default: the context's
+    last q_len tokens), so that any subset of a block's queries can be
+    evaluated on its own.  Returns (out [q_len, Hq, D] float64, lse
+    [q_len, Hq] float64).
     """
     q = np.asarray(q)
     q_len, hq, dim = q.shape
     ctx, hkv, _ = k.shape
-    assert hq % hkv == 0 and q_len <= ctx
+    assert hq % hkv == 0 and (positions is not None or q_len <= ctx)
     g = hq // hkv
-    vis = visible_mask(ctx, q_len, window_left, num_sinks, key_lo, key_hi)
+    vis = visible_mask(ctx, q_len, window_left, num_sinks, key_lo, key_hi, positions)
     cols = np.nonzero(vis.any(axis=0))[0]          # keys any query can see
     out = np.zeros((q_len, hq, dim), dtype=np.float64)
     lse = np.full((q_len, hq), -np.inf, dtype=np.float64)

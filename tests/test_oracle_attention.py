@@ -253,3 +253,46 @@ def test_merge_closed_form():
     pl = np.array([[0.0], [math.log(3.0)]])
     o, l = A.lse_merge(po, pl)
     assert abs(o[0, 0] - 5.0) < 1e-14 and abs(l[0] - math.log(4.0)) < 1e-14
+
+
+def test_explicit_positions_select_rows_of_the_block():
+    """Rows are independent: evaluating a subset of a block's queries at their
+    own positions gives exactly those rows of the whole block; the default
+    positions are the context's last q_len tokens."""
+    rng = np.random.default_rng(21)
+    ctx, q_len, hq, hkv, d = 90, 40, 4, 2, 8
+    q = rng.standard_normal((q_len, hq, d))
+    k = rng.standard_normal((ctx, hkv, d))
+    v = rng.standard_normal((ctx, hkv, d))
+    for w, sinks in [(-1, 0), (13, 3)]:
+        full_o, full_l = A.attention(q, k, v, 0.3, w, sinks)
+        pos = ctx - q_len + np.arange(q_len)
+        o, l = A.attention(q, k, v, 0.3, w, sinks, positions=pos)
+        assert np.array_equal(o, full_o) and np.array_equal(l, full_l)
+        sub = np.array([0, 7, 8, 31, 39])
+        o, l = A.attention(q[sub], k, v, 0.3, w, sinks, positions=pos[sub])
+        np.testing.assert_allclose(o, full_o[sub], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(l, full_l[sub], rtol=1e-12, atol=1e-14)
+
+
+def test_explicit_positions_match_brute_force():
+    """A query at position p sees keys 0..p (and with a window the last W plus
+    the sinks): brute force over explicit positions, including one before
+    every key of a window."""
+    rng = np.random.default_rng(22)
+    ctx, hq, hkv, d = 12, 2, 1, 3
+    k = rng.standard_normal((ctx, hkv, d))
+    v = rng.standard_normal((ctx, hkv, d))
+    positions = np.array([0, 3, 11, 20])
+    q = rng.standard_normal((positions.size, hq, d))
+    for w, sinks in [(-1, 0), (4, 2)]:
+        o, l = A.attention(q, k, v, 0.5, w, sinks, positions=positions)
+        for i, p in enumerate(positions):
+            keys = [j for j in range(ctx) if j <= p and (w < 0 or p - j < w or j < sinks)]
+            for h in range(hq):
+                s = np.array([0.5 * float(q[i, h] @ k[j, 0]) for j in keys])
+                m = s.max()
+                e = np.exp(s - m)
+                want = (e[:, None] * v[keys, 0]).sum(axis=0) / e.sum()
+                np.testing.assert_allclose(o[i, h], want, rtol=1e-12, atol=1e-14)
+                assert abs(l[i, h] - (m + np.log(e.sum()))) < 1e-12
