@@ -26,6 +26,7 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_HBM_GBS = 8000.0
+PEAK_F16_TFLOPS = 2500.0      # dense fp16 matrix-core peak (the path's MFMA dtype)
 POOL_ROTATION_BYTES = 1 << 30
 KERNEL_SOURCES = ["paged_quantized_kv_ra_amd/csrc/attn_mfma.hip",
                   "paged_quantized_kv_ra_amd/csrc/attn_common.h", "paged_quantized_kv_ra_amd/csrc/ra_device.h",
@@ -124,12 +125,20 @@ class Step:
                              w.window_left, w.num_sinks, w.num_splits, hkv, ks, vs)
             self.args.append(a)
         self.slots, po_n, _ = L.paged_attn_workspace(self.args[0])
+        # one partition slot (a long prefill chunk): the kernel writes out and
+        # lse itself and there is nothing to merge; otherwise partials only,
+        # and the merge is launched separately
+        self.direct = self.slots == 1
         self.po = torch.empty((self.slots, T, hq, D), dtype=torch.float32, device=dev)
         self.pl = torch.empty((self.slots, T, hq), dtype=torch.float32, device=dev)
-        for a in self.args:          # partials only: the merge is launched separately
-            a.partial_out = self.po.data_ptr()
-            a.partial_lse = self.pl.data_ptr()
-            a.partial_slots = self.slots
+        for a in self.args:
+            if self.direct:
+                a.out = self.out.data_ptr()
+                a.lse = self.lse.data_ptr()
+            else:
+                a.partial_out = self.po.data_ptr()
+                a.partial_lse = self.pl.data_ptr()
+                a.partial_slots = self.slots
         self.rows = T * hq
         self.q_code = L.RA_F16 if w.q_dtype == "f16" else L.RA_BF16
         self.kv_code = L.KV_CODES[w.kv_dtype]
@@ -172,8 +181,9 @@ class Step:
         st |= lib.ra_paged_attn(ctypes.byref(self.args[i % self.copies]), s)
         if ev is not None:
             ev[1].record()
-        st |= lib.ra_lse_merge(self.po.data_ptr(), self.pl.data_ptr(), self.slots, self.rows, w.head_dim,
-                               self.out.data_ptr(), self.q_code, self.lse.data_ptr(), s)
+        if not self.direct:
+            st |= lib.ra_lse_merge(self.po.data_ptr(), self.pl.data_ptr(), self.slots, self.rows, w.head_dim,
+                                   self.out.data_ptr(), self.q_code, self.lse.data_ptr(), s)
         if st != 0:
             raise RuntimeError(lib.ra_last_error().decode())
 
@@ -201,6 +211,8 @@ def cpu_baseline(w, seconds):
     except Exception:  # noqa: BLE001
         threads = 1
     g = w.num_q_heads // w.num_kv_heads
+    if w.meta.get("kind") == "prefill":
+        return cpu_baseline_prefill(w, seconds, threads, OA, OC)
     done_tokens, elapsed, seqs = 0, 0.0, 0
     b = 0
     codes = {}
@@ -224,6 +236,39 @@ def cpu_baseline(w, seconds):
     return {"value": done_tokens / elapsed, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{seqs} whole sequences (all {w.num_kv_heads} KV heads x {g} query heads) of "
                       f"{w.name}: dequantise + fp64 attention, {elapsed:.1f} s"}
+
+
+def cpu_baseline_prefill(w, seconds, threads, OA, OC):
+    """Prefill: the oracle on evenly spread chunks of sequence 0's queries
+    (each at its own position) until about `seconds` of CPU time, after
+    dequantising the sequence's K and V once (timed).  Reported as query
+    tokens per second of the whole step's mix."""
+    import numpy as np
+    rows = w.seq_rows[0]
+    ctx, ql = int(w.ctx[0]), int(w.q_len[0])
+    q_all = OC.source_to_f32(w.q[:ql], w.q_dtype).astype("float64")
+    kc = OC.quantize(OC.source_to_f32(w.tokens_k[rows], w.src_dtype), w.kv_dtype, w.k_scale)
+    vc = OC.quantize(OC.source_to_f32(w.tokens_v[rows], w.src_dtype), w.kv_dtype, w.v_scale)
+    t = time.perf_counter()
+    k = OC.dequantize(kc, w.kv_dtype, w.k_scale)
+    v = OC.dequantize(vc, w.kv_dtype, w.v_scale)
+    elapsed = time.perf_counter() - t
+    chunk = max(1, (1 << 24) // (w.num_q_heads * ctx))      # scores of one chunk: <= 2^24 fp64
+    order = np.random.default_rng(0).permutation(ql)
+    done, flops = 0, 0
+    vis = w.visible_per_query()[:ql]
+    while elapsed < seconds and done < ql:
+        sel = np.sort(order[done:done + chunk])
+        t = time.perf_counter()
+        OA.attention(q_all[sel], k, v, w.softmax_scale, w.window_left, w.num_sinks, positions=ctx - ql + sel)
+        elapsed += time.perf_counter() - t
+        done += sel.size
+        flops += int(vis[sel].sum()) * w.num_q_heads * 4 * w.head_dim
+    # scale the sampled queries' share of the work to the whole step
+    frac = flops / w.attention_flops()
+    return {"value": w.total_q * frac / elapsed, "unit": "query tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {ql} queries (random positions, all {w.num_q_heads} heads) of {w.name}: "
+                      f"dequantise + fp64 attention, {elapsed:.1f} s = {frac:.2%} of the step's flops"}
 
 
 def traffic_from_profile(wname, src_hash):
@@ -331,19 +376,34 @@ def main():
         ms_per_step, attn_avg_ms, wall = time_eager(step, args, torch)
     else:
         ms_per_step, attn_avg_ms, wall = time_graphs(step, args, torch)
+    prefill = w.meta.get("kind") == "prefill"
     tokens = w.attended_keys()
-    value = tokens / (ms_per_step / 1e3)
+    value = (w.total_q if prefill else tokens) / (ms_per_step / 1e3)
     alg = algorithmic_bytes(w)
+    flops = w.attention_flops()
     achieved = alg / (attn_avg_ms / 1e3) / 1e9
+    tflops = flops / (attn_avg_ms / 1e3) / 1e12
     src_hash = kernel_source_hash()
     traffic = traffic_from_profile(w.name, src_hash)
     log(f"{args.steps} steps ({'eager' if args.eager else 'graph replay'}): {ms_per_step * 1e3:.1f} us/step "
         f"(wall {wall / args.steps * 1e6:.1f} us/step), "
-        f"attention {attn_avg_ms * 1e3:.1f} us avg, {achieved:.0f} GB/s algorithmic")
+        f"attention {attn_avg_ms * 1e3:.1f} us avg, {achieved:.0f} GB/s algorithmic, {tflops:.1f} TFLOP/s")
+    if prefill:
+        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / PEAK_F16_TFLOPS, 4), "traffic": traffic, "kernel": "attn_mfma_kernel",
+                "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": alg,
+                "attn_us": round(attn_avg_ms * 1e3, 2), "kernel_source_hash": src_hash}
+    else:
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": traffic, "kernel": "attn_mfma_kernel",
+                "algorithmic_bytes_per_launch": alg, "attn_us": round(attn_avg_ms * 1e3, 2),
+                "kernel_source_hash": src_hash}
     line = {
-        "metric": "KV tokens attended/sec and achieved HBM GB/s (% of MI355X peak), FP8 KV @32K",
+        "metric": ("prefill query tokens/sec (paged attention, one layer), FP8 KV" if prefill else
+                   "KV tokens attended/sec and achieved HBM GB/s (% of MI355X peak), FP8 KV @32K"),
         "value": round(value, 1),
-        "unit": "tokens/s",
+        "unit": "query tokens/s" if prefill else "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -358,11 +418,7 @@ def main():
                    "kv_dtype": w.kv_dtype, "page_size": 16, "partition_slots": step.slots,
                    "kv_pool_copies": step.copies, "launch": "eager" if args.eager else "hip_graph",
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": traffic, "kernel": "attn_mfma_kernel",
-                     "algorithmic_bytes_per_launch": alg, "attn_us": round(attn_avg_ms * 1e3, 2),
-                     "kernel_source_hash": src_hash},
+        "roofline": roof,
         "attended_tokens_per_step": tokens,
     }
     if not args.no_cpu_baseline:

@@ -171,8 +171,17 @@ int32_t ra_kv_store_int8_token(const void* k, const void* v, int32_t src_dtype,
  *
  * Splitting: the keys of sequence b are cut into partitions of P_b tokens;
  * num_splits = S > 0 gives P_b = 16 * ceil(ceil(ctx_b / S) / 16) (S slots per
- * sequence); num_splits = 0 uses a fixed partition size chosen by the library
- * from the call's constants only (see ra_paged_attn_workspace).  With more than
+ * sequence); num_splits = 0 lets the library choose P_b from the sequence's
+ * own ctx_b and q_len_b and the head counts, never from the rest of the batch:
+ *   rows_b = (Hq / Hkv) * q_len_b < 16 (decode): about 32 partitions of ctx_b,
+ *     P_b clamped to [512, 2048] tokens;
+ *   rows_b >= 16: P_b = max(2048, 16 * ceil(ceil(ctx_b / n_b) / 16)) with
+ *     n_b = ceil(2048 / u_b) partitions wanted, u_b = Hkv * ceil(rows_b / 48)
+ *     workgroups per partition (n_b = 1 once u_b >= 2048: a long prefill
+ *     chunk is attended in one pass).
+ * The grid's slot count follows from max_context_len, max_q_len and
+ * min_q_len; a sequence whose q_len_b is below min_q_len is written as NaN.
+ * With more than
  * one partition slot the kernel writes partial_out [slots][total_q][Hq][D] and
  * partial_lse [slots][total_q][Hq] (fp32; out already normalised; an empty
  * partition writes out = 0, lse = -inf) and, if `out` is non-NULL, merges them

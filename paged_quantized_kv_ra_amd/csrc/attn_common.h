@@ -39,7 +39,12 @@ __device__ __forceinline__ int32_t partition_tokens(const AttnLaunch& a, int32_t
     const int32_t per = (ctx + a.num_splits - 1) / a.num_splits;
     return ((per + kPage - 1) / kPage) * kPage;
   }
-  if (rows >= kSmallUnitRows) return a.part_tokens;
+  if (rows >= kSmallUnitRows) {
+    const int32_t units = a.hkv * ((rows + kMfmaRowsPerBlock - 1) / kMfmaRowsPerBlock);
+    const int32_t want = units >= kFillUnits ? 1 : (kFillUnits + units - 1) / units;
+    const int32_t per = ((ctx + want - 1) / want + kPage - 1) / kPage * kPage;
+    return max(per, a.part_tokens);
+  }
   const int32_t per = (ctx + kSmallSplits - 1) / kSmallSplits;
   const int32_t p = ((per + kPage - 1) / kPage) * kPage;
   return min(max(p, a.part_small), a.part_tokens);
@@ -86,12 +91,16 @@ __device__ __forceinline__ bool key_visible(const AttnLaunch& a, const SeqFrame&
 }
 
 // Block index -> logical unit id.  Consecutive workgroups are dispatched to the
-// 8 XCDs round-robin; the remap places consecutive logical ids on one XCD so
-// units that read the same pages (the sequences of a shared prefix, the row
-// groups of one sequence) share that XCD's L2.  gridDim.x is a multiple of 8.
-__device__ __forceinline__ int64_t logical_block() {
-  const int64_t per_xcd = gridDim.x / 8;
+// 8 XCDs round-robin.  With one row group the remap places consecutive logical
+// ids on one XCD so units that read the same pages (the sequences of a shared
+// prefix) share that XCD's L2.  With several row groups (long query blocks,
+// whose causal row groups differ in work) the ids stay in dispatch order, so
+// that the heaviest-first order below is spread evenly over the XCDs.
+// gridDim.x is a multiple of 8.
+__device__ __forceinline__ int64_t logical_block(int32_t row_groups) {
   const int64_t bid = blockIdx.x;
+  if (row_groups > 1) return bid;
+  const int64_t per_xcd = gridDim.x / 8;
   return (bid % 8) * per_xcd + bid / 8;
 }
 
@@ -99,14 +108,16 @@ struct UnitId {
   int32_t b, h, s, rg;
 };
 
-// logical id = ((s * Hkv + h) * row_groups + rg) * batch + b
+// logical id = ((s * row_groups + (row_groups - 1 - rg)) * Hkv + h) * batch + b:
+// within a partition slot the last row group (the latest queries, which see
+// the most keys under the causal mask) comes first
 __device__ __forceinline__ bool decode_unit(const AttnLaunch& a, int32_t row_groups, UnitId& u) {
-  int64_t id = logical_block();
+  int64_t id = logical_block(row_groups);
   const int64_t total = (int64_t)a.slots * a.hkv * row_groups * a.batch;
   if (id >= total) return false;
   u.b = (int32_t)(id % a.batch); id /= a.batch;
-  u.rg = (int32_t)(id % row_groups); id /= row_groups;
   u.h = (int32_t)(id % a.hkv); id /= a.hkv;
+  u.rg = row_groups - 1 - (int32_t)(id % row_groups); id /= row_groups;
   u.s = (int32_t)id;
   return true;
 }
@@ -121,6 +132,7 @@ inline unsigned padded_grid(int64_t units) {
 __device__ __forceinline__ bool seq_ok(const AttnLaunch& a, int32_t ctx, int32_t q0, int32_t q1, int32_t kv0,
                                        int32_t qp0) {
   return ctx >= 0 && ctx <= a.max_ctx && q0 >= 0 && q1 >= q0 && q1 <= a.total_q && q1 - q0 <= a.max_q_len &&
+         q1 - q0 >= a.min_q_len &&
          (a.q_pos0 ? qp0 >= 0 : q1 - q0 <= ctx) && kv0 >= 0;
 }
 

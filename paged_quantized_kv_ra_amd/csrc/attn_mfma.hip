@@ -331,6 +331,12 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a,
   const int32_t qp0 = a.q_pos0 ? a.q_pos0[u.b] : 0;
   bool bad = !seq_ok(a, ctx, q0, q1, kv0, qp0);
   const SeqFrame fr = seq_frame(a, ctx, q_len, kv0, qp0);
+  // the row group's own queries i = row0 / g .. (last row) / g bound the keys
+  // it can see: a long block (chunked prefill) skips pages past its last query
+  // and masks only pages past its first
+  SeqFrame frg = fr;
+  frg.pmin = fr.pmin + row0 / g;
+  frg.pmax = fr.pmin + (min(row0 + kMfmaRowsPerBlock, rows) - 1) / g;
 
   // partition and visible pages
   int32_t lo = 0, hi = 0;
@@ -339,7 +345,7 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a,
     const int32_t P = partition_tokens(a, ctx, rows);
     lo = u.s * P;
     hi = min(lo + P, ctx);
-    pg = unit_pages(a, fr, lo, hi);
+    pg = unit_pages(a, frg, lo, hi);
   }
   const int32_t npages = pg.count();
   const int32_t* bt_row = a.block_tables + (int64_t)u.b * a.bt_stride;
@@ -432,7 +438,7 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a,
             wait_vmcnt<0>();
           PageRegs<KV, D> r;
           read_page<KV, D>(r, ring + j * G::NSL, scl + j * 32, lane_off, kgrp);
-          compute_page<KV, D, NT>(acc, r, qf, a, pg, ws.page(k), ctx, fr, pos, kgrp, c, thr);
+          compute_page<KV, D, NT>(acc, r, qf, a, pg, ws.page(k), ctx, frg, pos, kgrp, c, thr);
           // the slot's reads have returned (their values were consumed) before
           // the next load may overwrite it
           wait_lgkmcnt0();

@@ -109,7 +109,14 @@ int32_t check_attn(const ra_attn_args* a, Plan* plan) {
     // the partition size is chosen per sequence by its row count; the grid
     // holds enough slots for either kind the bounds admit
     int64_t s = 1;
-    if (rows_max >= ra::kSmallUnitRows) s = std::max<int64_t>(s, ceil_div(a->max_context_len, plan->part_large));
+    if (rows_max >= ra::kSmallUnitRows) {
+      // a sequence with rows >= kSmallUnitRows takes at most
+      // ceil(kFillUnits / (Hkv * its row groups)) partitions; the fewest row
+      // groups such a sequence can have bound them all
+      const int64_t rg_lo = ceil_div(std::max<int64_t>(rows_min, ra::kSmallUnitRows), ra::kMfmaRowsPerBlock);
+      const int64_t fill = ceil_div(ra::kFillUnits, a->num_kv_heads * rg_lo);
+      s = std::max<int64_t>(s, std::min<int64_t>(ceil_div(a->max_context_len, plan->part_large), fill));
+    }
     if (rows_min < ra::kSmallUnitRows) {
       // decode units: at most kSmallSplits partitions up to kSmallSplits * kAutoPartLarge
       // tokens, kAutoPartLarge-token partitions beyond
@@ -187,6 +194,7 @@ ra::AttnLaunch make_launch(const ra_attn_args* a, const Plan& p) {
   L.head_dim = a->head_dim;
   L.num_pages = a->num_pages;
   L.max_q_len = a->max_q_len;
+  L.min_q_len = a->min_q_len;
   L.max_ctx = a->max_context_len;
   L.softmax_scale = a->softmax_scale;
   L.window = a->window_left < 0 ? -1 : a->window_left;

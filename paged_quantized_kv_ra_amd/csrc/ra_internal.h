@@ -71,6 +71,7 @@ struct AttnLaunch {
   int32_t head_dim;
   int64_t num_pages;
   int32_t max_q_len;
+  int32_t min_q_len;     // host lower bound of every q_len (0: unknown); the grid's slot count relies on it
   int32_t max_ctx;
   float softmax_scale;
   int32_t window;        // < 0: none
@@ -92,7 +93,10 @@ struct AttnLaunch {
 constexpr int kMfmaRowsPerBlock = 48;   // rows beyond this split over row groups
 
 // Automatic partitions (num_splits = 0).  Units with at least kSmallUnitRows
-// rows use kAutoPartLarge tokens.  Smaller (decode) units take about
+// rows use kAutoPartLarge tokens, or more when the sequence's own row groups
+// already give kFillUnits workgroups or more across the KV heads (a long
+// prefill chunk): its keys are then cut into only as many partitions as it
+// takes to reach kFillUnits, down to one.  Smaller (decode) units take about
 // kSmallSplits partitions of their own sequence's context, clamped to
 // [kAutoPartSmall, kAutoPartLarge] tokens, so that a decode batch still fills
 // the chip while long contexts keep few partials.  Either rule depends only on
@@ -101,6 +105,7 @@ constexpr int kSmallUnitRows = 16;
 constexpr int kAutoPartLarge = 2048;
 constexpr int kAutoPartSmall = 512;
 constexpr int kSmallSplits = 32;
+constexpr int kFillUnits = 2048;
 
 hipError_t launch_attn_mfma(const AttnLaunch& a, hipStream_t s);
 

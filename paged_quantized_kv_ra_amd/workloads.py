@@ -137,6 +137,25 @@ class Workload:
         per_head = self.head_dim * self.elem_bytes + (4 if self.kv_dtype == "int8_tok" else 0)
         return self.attended_keys() * 2 * self.num_kv_heads * per_head
 
+    def visible_per_query(self):
+        """int64[T]: number of keys each query row sees (causal within the
+        block, window plus the sinks below it)."""
+        out = []
+        for b in range(self.batch):
+            c, ql = int(self.ctx[b]), int(self.q_len[b])
+            p = np.arange(c - ql, c, dtype=np.int64)          # query positions
+            if self.window_left < 0:
+                out.append(p + 1)
+            else:
+                w = self.window_left
+                out.append(np.minimum(p + 1, w) + np.minimum(self.num_sinks, np.maximum(0, p + 1 - w)))
+        return np.concatenate(out) if out else np.zeros(0, np.int64)
+
+    def attention_flops(self):
+        """Multiply-adds of QK^T and PV counted as 2 flops each: 4 * D per
+        (query head, visible key) pair."""
+        return int(self.visible_per_query().sum()) * self.num_q_heads * 4 * self.head_dim
+
     def unique_pages_attended(self):
         """Distinct physical pages touched (shared prefix pages counted once)."""
         pages = set()
@@ -308,6 +327,27 @@ def split_fp8_512k_sliding(base=None):
                  num_sinks=4, kv_source=base)
 
 
+def prefill_fp8_8k():
+    """Cold prefill of an 8K prompt: one sequence whose 8,192 tokens are all
+    queries, causal, E4M3 KV (ReVolta README, intro table, "Cold prompt 8K
+    tokens" prefill throughput)."""
+    w = build("prefill_e4m3_1x8k", 7, ctx=[8 * K], q_len=8 * K, num_q_heads=16, num_kv_heads=2,
+              head_dim=128, kv_dtype="e4m3", q_dtype="f16", pool_pages=1024)
+    w.meta["kind"] = "prefill"
+    return w
+
+
+def chunk_prefill_fp8_128k():
+    """One chunk of a 131,072-token cold prompt: the last 4,896 tokens (the
+    long-prefill token threshold of the recommended launch flags) attending
+    to the whole prompt, E4M3 KV (ReVolta README, intro table, "Cold prompt
+    131K tokens"; "Quick start" launch flags)."""
+    w = build("chunk_prefill_e4m3_1x128k_q4896", 8, ctx=[128 * K], q_len=4896, num_q_heads=16,
+              num_kv_heads=2, head_dim=128, kv_dtype="e4m3", q_dtype="f16", pool_pages=8704)
+    w.meta["kind"] = "prefill"
+    return w
+
+
 BENCH_WORKLOADS = {
     "tiny_decode": tiny_decode,
     "batch8_decode": batch8_decode,
@@ -317,4 +357,6 @@ BENCH_WORKLOADS = {
     "prefix_int8_256k": prefix_int8_256k,
     "split_fp8_512k": split_fp8_512k,
     "split_fp8_512k_sliding": split_fp8_512k_sliding,
+    "prefill_fp8_8k": prefill_fp8_8k,
+    "chunk_prefill_fp8_128k": chunk_prefill_fp8_128k,
 }

@@ -82,8 +82,9 @@ def q_f64(w, b):
     return OC.source_to_f32(w.q[q0:q1], w.q_dtype).astype(np.float64)
 
 
-def oracle_seq(w, b, kv_heads=None):
-    """Oracle (out, lse) of sequence b for the query heads of the given KV heads."""
+def oracle_seq(w, b, kv_heads=None, q_rows=None):
+    """Oracle (out, lse) of sequence b for the query heads of the given KV heads
+    (and only the block's queries q_rows, each at its own position)."""
     hkv = w.num_kv_heads
     g = w.num_q_heads // hkv
     heads = list(range(hkv)) if kv_heads is None else list(kv_heads)
@@ -91,8 +92,13 @@ def oracle_seq(w, b, kv_heads=None):
     k = dequant_tokens(w, rows, "k", heads)
     v = dequant_tokens(w, rows, "v", heads)
     q = q_f64(w, b)
+    pos = None
+    if q_rows is not None:
+        q_rows = np.asarray(q_rows, dtype=np.int64)
+        q = q[q_rows]
+        pos = int(w.ctx[b]) - int(w.q_len[b]) + q_rows
     qh = np.concatenate([q[:, h * g:(h + 1) * g] for h in heads], axis=1)
-    return OA.attention(qh, k, v, w.softmax_scale, w.window_left, w.num_sinks)
+    return OA.attention(qh, k, v, w.softmax_scale, w.window_left, w.num_sinks, positions=pos)
 
 
 def qhead_cols(w, kv_heads):

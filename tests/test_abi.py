@@ -177,6 +177,16 @@ def test_fp16_cache_ignores_scales_and_workspace_query():
     for ctx, slots in [(5000, 10), (16384, 32), (40000, 32), (65536, 32), (100000, 49)]:
         a = _good_args(L, num_splits=0, max_q_len=1, min_q_len=1, block_table_stride=7000, max_context_len=ctx)
         assert L.paged_attn_workspace(a)[0] == slots, ctx
+    # long query blocks (16 query heads over 2 KV heads, 48 rows per row group):
+    # 2048-token partitions until the row groups alone give 2048 workgroups
+    for ctx, ql, qmin, slots in [(32768, 5, 5, 16),        # verify: 1 row group -> 2048-token partitions
+                                 (8192, 8192, 8192, 1),    # 2 x 1366 row groups >= 2048: one pass, direct
+                                 (8192, 8192, 0, 16),      # min_q_len unknown: a decode sequence may take 16 x 512
+                                 (131072, 4896, 4896, 2),  # 2 x 816 row groups: ceil(2048 / 1632) = 2
+                                 (131072, 512, 6, 64)]:    # a 6-query block (1 row group) keeps 64 x 2048
+        a = _good_args(L, num_splits=0, max_q_len=ql, min_q_len=qmin, total_q=ql, block_table_stride=8192,
+                       max_context_len=ctx)
+        assert L.paged_attn_workspace(a)[0] == slots, (ctx, ql, qmin)
 
 
 def test_empty_batch_is_ok_without_pointers():

@@ -44,6 +44,15 @@ CASES = [
     ("mfma_g8_q5_int8tok", [1000, 77, 513, 40], 5, 16, 2, 128, "int8_tok", "f16", -1, 0, 3),
     ("dec_g8_int8tok_auto", [3000, 77, 513], 1, 16, 2, 128, "int8_tok", "bf16", -1, 0, 0),
     ("mfma_g8_q16_int8tok_window_d64", [900, 300], 16, 16, 2, 64, "int8_tok", "f16", 100, 4, 2),
+    # prefill: long query blocks over many row groups (cold prompts with
+    # q_len = ctx, and chunks after a cached prefix), causal page skipping
+    ("pre_g8_e4m3_cold", [700, 300, 33], [700, 300, 33], 16, 2, 128, "e4m3", "f16", -1, 0, 0),
+    ("pre_g8_int8_chunk_auto_bf16q", [3000, 1500], [600, 250], 16, 2, 128, "int8", "bf16", -1, 0, 0),
+    ("pre_g8_e4m3_chunk_split5", [2000, 999], [400, 999], 16, 2, 128, "e4m3", "f16", -1, 0, 5),
+    ("pre_g8_e4m3_window_sinks", [1500, 400], [500, 400], 16, 2, 128, "e4m3", "f16", 128, 4, 0),
+    ("pre_g4_int8tok_d64", [640, 333], [640, 100], 8, 2, 64, "int8_tok", "f16", -1, 0, 0),
+    ("pre_g1_f16_direct", [500, 129], [500, 129], 4, 4, 128, "f16", "f16", -1, 0, 1),
+    ("mixed_decode_prefill", [900, 1200, 64], [1, 300, 64], 16, 2, 128, "e4m3", "f16", -1, 0, 0),
 ]
 
 
@@ -140,7 +149,8 @@ def _single(w, b):
     return q0, q1
 
 
-@pytest.mark.parametrize("case", [CASES[1], CASES[8], CASES[14], CASES[17], CASES[22], CASES[24]], ids=lambda c: c[0])
+@pytest.mark.parametrize("case", [CASES[1], CASES[8], CASES[14], CASES[17], CASES[22], CASES[24], CASES[27],
+                                  CASES[32]], ids=lambda c: c[0])
 def test_batch_invariance_bitwise(case):
     """A sequence's result does not depend on the rest of the batch (other
     lengths change the automatic split count, and mixing decode with verify

@@ -28,7 +28,23 @@ CONFIGS = [
     # beyond the five: plain decode at 32K, and per-token INT8 at the verify shape
     ("decode_fp8_32k", W.decode_fp8_32k, [(2, 1)]),
     ("verify_int8tok_32k", W.verify_int8tok_32k, [(0, 1), (6, 0)]),
+    # prefill: sampled query rows (row-group edges, the first and last queries,
+    # random ones) of each sampled KV head
+    ("prefill_fp8_8k", W.prefill_fp8_8k, [(0, 0, "sample"), (0, 1, "sample")]),
+    ("chunk_prefill_fp8_128k", W.chunk_prefill_fp8_128k, [(0, 1, "sample")]),
 ]
+
+
+def _query_sample(w, b, seed):
+    """Query rows of sequence b: the first and last, both sides of several
+    48-row group edges (6 queries of 8 heads each), and random ones."""
+    ql = int(w.q_len[b])
+    g = w.num_q_heads // w.num_kv_heads
+    per_group = 48 // g if 48 % g == 0 else 1
+    edges = [e for k in (1, 2, ql // per_group // 2, ql // per_group - 1) for e in (k * per_group - 1, k * per_group)]
+    rng = np.random.default_rng(seed)
+    rows = np.concatenate([[0, ql - 1], edges, rng.integers(0, ql, size=24)])
+    return np.unique(np.clip(rows, 0, ql - 1))
 
 
 def _check_store_sample(w, dw, n=48, seed=0):
@@ -73,12 +89,14 @@ def _run(name, make, units, base=None):
         torch.cuda.synchronize()
     out = out_to_np(out)
     lse = lse.cpu().numpy().astype(np.float64)
-    for b, h in units:
+    for unit in units:
+        b, h = unit[:2]
         q0, q1 = int(w.query_start_loc[b]), int(w.query_start_loc[b + 1])
         cols = qhead_cols(w, [h])
-        with Timer(f"{name}: oracle seq {b} kv head {h}"):
-            ro, rl = oracle_seq(w, b, kv_heads=[h])
-        e = compare(out[q0:q1][:, cols], lse[q0:q1][:, cols], ro, rl, f"{name} seq {b} head {h}")
+        q_rows = _query_sample(w, b, seed=h) if len(unit) > 2 else np.arange(q1 - q0)
+        with Timer(f"{name}: oracle seq {b} kv head {h}, {q_rows.size} queries"):
+            ro, rl = oracle_seq(w, b, kv_heads=[h], q_rows=q_rows if len(unit) > 2 else None)
+        e = compare(out[q0:q1][q_rows][:, cols], lse[q0:q1][q_rows][:, cols], ro, rl, f"{name} seq {b} head {h}")
         log(f"{name} seq {b} head {h}: max abs {e[0]:.2e} normwise {e[1]:.2e} lse {e[2]:.2e}")
     assert np.isfinite(out).all()
     return w
