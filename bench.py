@@ -13,8 +13,14 @@ Output: one JSON line.  `value` is KV tokens attended per second over the
 timed steps; `roofline` is the attention kernel's algorithmic HBM bytes per
 launch over its average duration (HIP events on the launch stream);
 `cpu_baseline` is the CPU oracle timed on a bounded sample of the same step.
+Prefill workloads (whole prompts or prompt chunks as the query block) report
+query tokens per second instead, and an MFMA roofline in TFLOP/s (4 * D
+flops per visible (query head, key) pair); with one partition slot the
+attention writes its output directly and there is no merge.
+``--fused-qkv`` stores the new tokens from packed QKV rows with RoPE
+(ra_qkv_rope_store, which also writes the rotated Q) instead of ra_kv_store.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--fused-qkv] [--gpus 1]
 """
 import argparse
 import ctypes
@@ -54,6 +60,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fused-qkv", action="store_true",
+                    help="store the new tokens with ra_qkv_rope_store (packed QKV rows, RoPE with YaRN "
+                         "factor 2, Q written for attention) instead of ra_kv_store")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from the host instead of replaying captured HIP graphs")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -78,7 +87,7 @@ def copy_calibration():
 class Step:
     """Device state and prebuilt C-ABI argument blocks for one workload."""
 
-    def __init__(self, w):
+    def __init__(self, w, fused_qkv=False):
         import torch
         import paged_quantized_kv_ra_amd as P
         from paged_quantized_kv_ra_amd import _lib as L
@@ -142,6 +151,20 @@ class Step:
         self.rows = T * hq
         self.q_code = L.RA_F16 if w.q_dtype == "f16" else L.RA_BF16
         self.kv_code = L.KV_CODES[w.kv_dtype]
+        self.rope_args = None
+        if fused_qkv:
+            # packed QKV rows of the new tokens (fp16), their positions, and
+            # the library's YaRN table (factor 2 over half the positions used)
+            from paged_quantized_kv_ra_amd import workloads as W
+            assert w.q_dtype == "f16" and self.k_new.shape[0] == T
+            pos, slots = W.step_positions_and_slots(w)
+            self.qkv = self._src(W.packed_qkv(w.seed, T, hq, hkv, D, "f16"))
+            self.positions = torch.from_numpy(pos).to(dev)
+            max_pos = int(pos.max()) + 1
+            self.table = P.rope_table(max_pos, D, 1e6, 2.0, max(1, max_pos // 2), device=dev)
+            self.rope_args = [L._rope_args(self.qkv, self.positions, self.table, D, hq, hkv, D, self.q,
+                                           self.slots_new, k, v, w.kv_dtype, w.k_scale, w.v_scale, ks, vs)
+                              for k, v, ks, vs in self.pools]
 
     @staticmethod
     def _src(x):
@@ -166,7 +189,9 @@ class Step:
         w, lib, L = self.w, self.lib, self.L
         k, v, ks, vs = self.pools[i % self.copies]
         s = ctypes.c_void_p(stream)
-        if ks is not None:
+        if self.rope_args is not None:
+            st = lib.ra_qkv_rope_store(ctypes.byref(self.rope_args[i % self.copies]), s)
+        elif ks is not None:
             st = lib.ra_kv_store_int8_token(self.k_new.data_ptr(), self.v_new.data_ptr(), L.RA_F16,
                                             self.k_new.stride(0), self.v_new.stride(0), self.slots_new.data_ptr(),
                                             self.k_new.shape[0], k.data_ptr(), v.data_ptr(), ks.data_ptr(),
@@ -370,7 +395,7 @@ def main():
     t0 = time.time()
     w = make()
     log(f"built {w.name} in {time.time() - t0:.1f}s")
-    step = Step(w)
+    step = Step(w, fused_qkv=args.fused_qkv)
     log(f"pool copies: {step.copies}, partition slots: {step.slots}")
     if args.eager:
         ms_per_step, attn_avg_ms, wall = time_eager(step, args, torch)
@@ -417,6 +442,7 @@ def main():
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "kv_dtype": w.kv_dtype, "page_size": 16, "partition_slots": step.slots,
                    "kv_pool_copies": step.copies, "launch": "eager" if args.eager else "hip_graph",
+                   "store": "qkv_rope_store" if args.fused_qkv else "kv_store",
                    "parallelism": "single GPU"},
         "roofline": roof,
         "attended_tokens_per_step": tokens,

@@ -10,7 +10,11 @@
  *                   tokens, causal inside the block, grouped query heads) over
  *                   its paged, quantised context, optionally split into KV
  *                   partitions that emit partial (out, lse) pairs;
- *   ra_lse_merge    combine partial (out, lse) pairs by log-sum-exp.
+ *   ra_lse_merge    combine partial (out, lse) pairs by log-sum-exp;
+ *   ra_qkv_rope_store  one pass over the new tokens' packed QKV rows: rotary
+ *                   position embedding of Q and K (YaRN table), Q written
+ *                   for attention, K/V quantised into the pages;
+ *   ra_rope_table   (host) the RoPE / YaRN cos-sin table it reads.
  *
  * Sources of the operations (the ReVolta pages):
  *   - ReVolta README, intro list and "Weight and KV formats": the KV cache is
@@ -84,7 +88,7 @@
 extern "C" {
 #endif
 
-#define RA_KV_ABI_VERSION 2
+#define RA_KV_ABI_VERSION 3
 #define RA_KV_LAYOUT_ID 1
 #define RA_KV_PAGE_SIZE 16
 #define RA_KV_MAX_SPLITS 4096
@@ -146,6 +150,84 @@ int32_t ra_kv_store_int8_token(const void* k, const void* v, int32_t src_dtype,
                                void* k_cache, void* v_cache, float* k_scales, float* v_scales,
                                int64_t num_pages, int32_t num_kv_heads, int32_t head_dim,
                                int32_t page_size, void* stream);
+
+/*
+ * ra_rope_table -- (host only; enqueues nothing) fill the HOST buffer
+ * out [max_position][2][rotary_dim / 2] fp32 with cos(p * f_i) and
+ * sin(p * f_i) times the attention temperature m, computed in double and
+ * rounded once.  Plain RoPE (factor <= 1): f_i = base^(-2 i / rotary_dim),
+ * m = 1.  YaRN (factor > 1; ReVolta README, "Quick start", step 2: factor 2
+ * over original_max_position = 262,144 positions): with
+ * d(beta) = rotary_dim * ln(original_max_position / (2 pi beta)) / (2 ln base),
+ * lo = max(floor(d(beta_fast)), 0), hi = min(ceil(d(beta_slow)), rotary_dim - 1)
+ * and ramp_i = clamp((i - lo) / (hi - lo), 0, 1):
+ * f_i = base^(-2 i / rotary_dim) * (1 - ramp_i + ramp_i / factor) and
+ * m = 0.1 ln(factor) + 1.  (beta_fast = 32, beta_slow = 1 are the usual
+ * values.)  rotary_dim even and > 0; max_position >= 1; base > 1.  Copy the
+ * table to device memory for ra_qkv_rope_store.
+ */
+int32_t ra_rope_table(float* out, int32_t max_position, int32_t rotary_dim, double base,
+                      double factor, int32_t original_max_position, double beta_fast,
+                      double beta_slow);
+
+/*
+ * Arguments of ra_qkv_rope_store.  Set struct_size = sizeof(ra_qkv_rope_args).
+ *
+ * qkv         [num_tokens] rows of (num_q_heads + 2 * num_kv_heads) * head_dim
+ *             src_dtype elements (RA_F16 or RA_BF16): Q heads, then K heads,
+ *             then V heads, as a fused QKV projection writes them; rows are
+ *             qkv_token_stride ELEMENTS apart.
+ * positions   int64 [num_tokens]: each token's position in its sequence.
+ * rope_table  fp32 [max_position][2][rotary_dim / 2] (see ra_rope_table).
+ *             rotary_dim is a multiple of 16 and <= head_dim; dim i < R/2
+ *             pairs with dim i + R/2 (R = rotary_dim) and the pair turns as
+ *             y_i = x_i cos - x_{i+R/2} sin, y_{i+R/2} = x_{i+R/2} cos + x_i sin,
+ *             in fp32 without fused multiply-add; dims >= R pass through.
+ * q_out       [num_tokens][num_q_heads][head_dim] src_dtype (rounded to
+ *             nearest even), rows q_token_stride ELEMENTS apart: the rotated
+ *             queries, ready for ra_paged_attn.
+ * slot_mapping, k_cache, v_cache, kv_dtype, k_scale, v_scale, k_scales,
+ *             v_scales, num_pages: as ra_kv_store (per-layer scales for E4M3 /
+ *             INT8, scale planes for RA_KV_INT8_TOKEN, neither for FP16); the
+ *             rotated K rows and the V rows are quantised and stored exactly
+ *             as ra_kv_store stores fp32 values.
+ * head_dim in {64, 128}; page_size 16.  qkv, q_out, rope_table, the caches
+ * and the planes are 16-byte aligned; strides are multiples of 8.  A token
+ * whose position is outside [0, max_position) gets a NaN Q row and stores
+ * nothing; slot < 0 (or >= num_pages * 16) stores nothing, Q is still
+ * written.  One call handles at most 2^30 / ((num_q_heads + 2 *
+ * num_kv_heads) * head_dim / 16) tokens.
+ * (ReVolta README, DFlash2 settings list: the verifier's Q/K/V rows packed
+ * by one copy kernel; "Quick start", step 2: YaRN position scaling.)
+ */
+typedef struct ra_qkv_rope_args {
+  uint32_t struct_size;
+  const void* qkv;
+  int32_t src_dtype;
+  int64_t qkv_token_stride;
+  int64_t num_tokens;
+  const int64_t* positions;
+  const float* rope_table;
+  int32_t max_position;
+  int32_t rotary_dim;
+  void* q_out;
+  int64_t q_token_stride;
+  const int64_t* slot_mapping;
+  void* k_cache;
+  void* v_cache;
+  int32_t kv_dtype;
+  float k_scale;
+  float v_scale;
+  float* k_scales;
+  float* v_scales;
+  int64_t num_pages;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+} ra_qkv_rope_args;
+
+int32_t ra_qkv_rope_store(const ra_qkv_rope_args* args, void* stream);
 
 /*
  * Arguments of ra_paged_attn.  Set struct_size = sizeof(ra_attn_args).

@@ -7,7 +7,8 @@ at once (there is no fallback).
 """
 
 __all__ = ["kv_store", "paged_attn", "lse_merge", "kv_gather_dequant",
-           "paged_attn_workspace", "abi_version", "load_library", "new_cache", "new_scale_plane", "RaError"]
+           "paged_attn_workspace", "abi_version", "load_library", "new_cache", "new_scale_plane", "RaError",
+           "rope_table", "qkv_rope_store"]
 
 
 def __getattr__(name):

@@ -69,6 +69,36 @@ class AttnArgs(_c.Structure):
     ]
 
 
+class RopeArgs(_c.Structure):
+    """Mirror of ra_qkv_rope_args."""
+    _fields_ = [
+        ("struct_size", _c.c_uint32),
+        ("qkv", _vp),
+        ("src_dtype", _c.c_int32),
+        ("qkv_token_stride", _c.c_int64),
+        ("num_tokens", _c.c_int64),
+        ("positions", _vp),
+        ("rope_table", _vp),
+        ("max_position", _c.c_int32),
+        ("rotary_dim", _c.c_int32),
+        ("q_out", _vp),
+        ("q_token_stride", _c.c_int64),
+        ("slot_mapping", _vp),
+        ("k_cache", _vp),
+        ("v_cache", _vp),
+        ("kv_dtype", _c.c_int32),
+        ("k_scale", _c.c_float),
+        ("v_scale", _c.c_float),
+        ("k_scales", _vp),
+        ("v_scales", _vp),
+        ("num_pages", _c.c_int64),
+        ("num_q_heads", _c.c_int32),
+        ("num_kv_heads", _c.c_int32),
+        ("head_dim", _c.c_int32),
+        ("page_size", _c.c_int32),
+    ]
+
+
 EXPORTED = {
     "ra_kv_store": (_c.c_int32, [_vp, _vp, _c.c_int32, _c.c_int64, _c.c_int64, _vp, _c.c_int64, _vp, _vp,
                                  _c.c_int32, _c.c_int64, _c.c_int32, _c.c_int32, _c.c_int32, _c.c_float,
@@ -81,6 +111,9 @@ EXPORTED = {
     "ra_lse_merge": (_c.c_int32, [_vp, _vp, _c.c_int32, _c.c_int64, _c.c_int32, _vp, _c.c_int32, _vp, _vp]),
     "ra_kv_gather_dequant": (_c.c_int32, [_vp, _c.c_int32, _c.c_int32, _c.c_float, _vp, _vp, _c.c_int32,
                                           _c.c_int64, _c.c_int32, _c.c_int32, _vp, _vp]),
+    "ra_rope_table": (_c.c_int32, [_vp, _c.c_int32, _c.c_int32, _c.c_double, _c.c_double, _c.c_int32,
+                                   _c.c_double, _c.c_double]),
+    "ra_qkv_rope_store": (_c.c_int32, [_c.POINTER(RopeArgs), _vp]),
     "ra_last_error": (_c.c_char_p, []),
     "ra_abi_version": (_c.c_int32, []),
 }
@@ -286,3 +319,64 @@ def kv_gather_dequant(cache, which, kv_dtype, scale, block_table_row, ctx, head_
                                                _ptr(block_table_row), ctx, cache.shape[0], hkv, head_dim,
                                                _ptr(out), _stream(stream)))
     return out
+
+
+def rope_table(max_position, rotary_dim, base, factor=1.0, original_max_position=0, beta_fast=32.0,
+               beta_slow=1.0, device="cuda"):
+    """The library's RoPE / YaRN table [max_position][2][rotary_dim / 2] fp32,
+    built on the host and copied to `device` (None: keep the host tensor)."""
+    t = torch.empty((max_position, 2, rotary_dim // 2), dtype=torch.float32)
+    _check(load_library().ra_rope_table(_vp(t.data_ptr()), max_position, rotary_dim, float(base), float(factor),
+                                        int(original_max_position), float(beta_fast), float(beta_slow)))
+    return t if device is None else t.to(device)
+
+
+def _rope_args(qkv, positions, table, rotary_dim, num_q_heads, num_kv_heads, head_dim, q_out, slot_mapping,
+               k_cache, v_cache, kv_dtype, k_scale, v_scale, k_scales, v_scales):
+    a = RopeArgs()
+    a.struct_size = _c.sizeof(RopeArgs)
+    a.qkv = qkv.data_ptr()
+    a.src_dtype = _src_code(qkv)
+    a.qkv_token_stride = qkv.stride(0)
+    a.num_tokens = qkv.shape[0]
+    a.positions = positions.data_ptr()
+    a.rope_table = table.data_ptr()
+    a.max_position = table.shape[0]
+    a.rotary_dim = int(rotary_dim)
+    a.q_out = q_out.data_ptr()
+    a.q_token_stride = q_out.stride(0)
+    a.slot_mapping = slot_mapping.data_ptr()
+    a.k_cache = k_cache.data_ptr()
+    a.v_cache = v_cache.data_ptr()
+    a.kv_dtype = KV_CODES[kv_dtype]
+    a.k_scale = float(k_scale)
+    a.v_scale = float(v_scale)
+    a.k_scales = None if k_scales is None else k_scales.data_ptr()
+    a.v_scales = None if v_scales is None else v_scales.data_ptr()
+    a.num_pages = k_cache.shape[0]
+    a.num_q_heads = num_q_heads
+    a.num_kv_heads = num_kv_heads
+    a.head_dim = head_dim
+    a.page_size = PAGE
+    return a
+
+
+def qkv_rope_store(qkv, positions, table, slot_mapping, k_cache, v_cache, kv_dtype, *, num_q_heads,
+                   rotary_dim=None, k_scale=1.0, v_scale=1.0, k_scales=None, v_scales=None, q_out=None,
+                   stream=None):
+    """Packed QKV rows [T][(Hq + 2 Hkv) * D] -> rotated Q [T][Hq][D] (returned),
+    rotated K and V stored into the caches at slot_mapping."""
+    T = qkv.shape[0]
+    hkv = k_cache.shape[1]
+    D = k_cache.shape[2] // PAGE
+    assert qkv.stride(-1) == 1 and qkv.shape[1] >= (num_q_heads + 2 * hkv) * D
+    assert positions.dtype == torch.int64 and slot_mapping.dtype == torch.int64
+    assert table.dtype == torch.float32 and table.is_contiguous()
+    rot = table.shape[2] * 2 if rotary_dim is None else rotary_dim
+    assert table.shape[1] == 2 and table.shape[2] * 2 == rot
+    if q_out is None:
+        q_out = torch.empty((T, num_q_heads, D), dtype=qkv.dtype, device=qkv.device)
+    a = _rope_args(qkv, positions, table, rot, num_q_heads, hkv, D, q_out, slot_mapping, k_cache, v_cache,
+                   kv_dtype, k_scale, v_scale, k_scales, v_scales)
+    _check(load_library().ra_qkv_rope_store(_c.byref(a), _stream(stream)))
+    return q_out

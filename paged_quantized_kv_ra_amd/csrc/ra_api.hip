@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <string>
+#include <vector>
 
 #include "ra_internal.h"
 #include "ra_kv.h"
@@ -350,6 +351,103 @@ int32_t ra_kv_gather_dequant(const void* cache, int32_t which, int32_t kv_dtype,
                      ctx, num_pages, num_kv_heads, head_dim, out, scales};
   const hipError_t e = ra::launch_kv_gather(G, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(RA_ERR_HIP, "ra_kv_gather_dequant: launch failed: %s", hipGetErrorString(e));
+  return RA_OK;
+}
+
+int32_t ra_rope_table(float* out, int32_t max_position, int32_t rotary_dim, double base, double factor,
+                      int32_t original_max_position, double beta_fast, double beta_slow) {
+  if (!out) return fail(RA_ERR_INVALID_ARG, "ra_rope_table: out must be non-NULL");
+  if (max_position < 1 || rotary_dim < 2 || rotary_dim % 2)
+    return fail(RA_ERR_INVALID_ARG, "ra_rope_table: max_position >= 1 and an even rotary_dim >= 2 required");
+  if (!(std::isfinite(base) && base > 1.0) || !std::isfinite(factor))
+    return fail(RA_ERR_INVALID_ARG, "ra_rope_table: base must be finite and > 1, factor finite");
+  const bool yarn = factor > 1.0;
+  if (yarn && !(original_max_position >= 1 && std::isfinite(beta_fast) && std::isfinite(beta_slow) &&
+                beta_fast > 0.0 && beta_slow > 0.0))
+    return fail(RA_ERR_INVALID_ARG, "ra_rope_table: YaRN needs original_max_position >= 1 and positive betas");
+  const int half = rotary_dim / 2;
+  double lo = 0.0, hi = 1.0;
+  if (yarn) {
+    // the dim whose wavelength fits `beta` times into the original context
+    const auto dim_for = [&](double beta) {
+      return rotary_dim * std::log(original_max_position / (beta * 2.0 * M_PI)) / (2.0 * std::log(base));
+    };
+    lo = std::max(std::floor(dim_for(beta_fast)), 0.0);
+    hi = std::min(std::ceil(dim_for(beta_slow)), (double)(rotary_dim - 1));
+    if (hi == lo) hi = lo + 0.001;
+  }
+  const double temp = yarn ? 0.1 * std::log(factor) + 1.0 : 1.0;
+  std::vector<double> freq(half);
+  for (int i = 0; i < half; ++i) {
+    const double f = std::pow(base, -2.0 * i / rotary_dim);
+    const double ramp = yarn ? std::min(std::max((i - lo) / (hi - lo), 0.0), 1.0) : 0.0;
+    freq[i] = f * (1.0 - ramp) + (f / (yarn ? factor : 1.0)) * ramp;
+  }
+  for (int64_t p = 0; p < max_position; ++p) {
+    float* row = out + p * rotary_dim;
+    for (int i = 0; i < half; ++i) {
+      const double ang = (double)p * freq[i];
+      row[i] = (float)(std::cos(ang) * temp);
+      row[half + i] = (float)(std::sin(ang) * temp);
+    }
+  }
+  return RA_OK;
+}
+
+int32_t ra_qkv_rope_store(const ra_qkv_rope_args* a, void* stream) {
+  const char* fn = "ra_qkv_rope_store";
+  if (!a) return fail(RA_ERR_INVALID_ARG, "%s: args is NULL", fn);
+  if (a->struct_size < sizeof(ra_qkv_rope_args))
+    return fail(RA_ERR_INVALID_ARG, "%s: struct_size %u < %zu (ABI %d)", fn, a->struct_size,
+                sizeof(ra_qkv_rope_args), RA_KV_ABI_VERSION);
+  if (a->num_tokens < 0) return fail(RA_ERR_INVALID_ARG, "%s: num_tokens must be >= 0", fn);
+  if (a->src_dtype != RA_F16 && a->src_dtype != RA_BF16)
+    return fail(RA_ERR_UNSUPPORTED, "%s: src_dtype %d is not RA_F16 or RA_BF16", fn, a->src_dtype);
+  if (kv_kind(a->kv_dtype) < 0) return fail(RA_ERR_UNSUPPORTED, "%s: unknown kv_dtype %d", fn, a->kv_dtype);
+  if (a->head_dim != 64 && a->head_dim != 128)
+    return fail(RA_ERR_UNSUPPORTED, "%s: head_dim %d is not 64 or 128", fn, a->head_dim);
+  if (a->page_size != RA_KV_PAGE_SIZE)
+    return fail(RA_ERR_UNSUPPORTED, "%s: page_size %d is not 16", fn, a->page_size);
+  if (a->num_q_heads < 1 || a->num_kv_heads < 1)
+    return fail(RA_ERR_INVALID_ARG, "%s: num_q_heads and num_kv_heads must be >= 1", fn);
+  if (a->num_pages < 1) return fail(RA_ERR_INVALID_ARG, "%s: num_pages must be >= 1", fn);
+  if (a->rotary_dim < 16 || a->rotary_dim % 16 || a->rotary_dim > a->head_dim)
+    return fail(RA_ERR_INVALID_ARG, "%s: rotary_dim %d must be a multiple of 16 in [16, head_dim]", fn,
+                a->rotary_dim);
+  if (a->max_position < 1) return fail(RA_ERR_INVALID_ARG, "%s: max_position must be >= 1", fn);
+  if (per_layer_scales(a->kv_dtype) && !(good_scale(a->k_scale) && good_scale(a->v_scale)))
+    return fail(RA_ERR_INVALID_ARG,
+                "%s: %s KV needs finite positive per-layer k_scale and v_scale (got %g, %g); "
+                "there is no fallback scale", fn, kv_name(a->kv_dtype), (double)a->k_scale, (double)a->v_scale);
+  const int64_t h3 = (int64_t)a->num_q_heads + 2 * (int64_t)a->num_kv_heads;
+  if (a->qkv_token_stride < h3 * a->head_dim)
+    return fail(RA_ERR_INVALID_ARG, "%s: qkv_token_stride %lld smaller than (Hq + 2 Hkv) * head_dim", fn,
+                (long long)a->qkv_token_stride);
+  if (a->q_token_stride < (int64_t)a->num_q_heads * a->head_dim)
+    return fail(RA_ERR_INVALID_ARG, "%s: q_token_stride %lld smaller than num_q_heads * head_dim", fn,
+                (long long)a->q_token_stride);
+  if (a->num_tokens > (int64_t)(1 << 30) / (h3 * (a->head_dim / 16)))
+    return fail(RA_ERR_INVALID_ARG, "%s: num_tokens * (Hq + 2 Hkv) * head_dim / 16 must not exceed 2^30; "
+                "call in chunks", fn);
+  if (a->num_tokens == 0) return RA_OK;
+  if (!a->qkv || !a->positions || !a->rope_table || !a->q_out || !a->slot_mapping || !a->k_cache || !a->v_cache)
+    return fail(RA_ERR_INVALID_ARG, "%s: qkv, positions, rope_table, q_out, slot_mapping, k_cache and v_cache "
+                "must be non-NULL", fn);
+  const bool tok = a->kv_dtype == RA_KV_INT8_TOKEN;
+  if (tok && (!a->k_scales || !a->v_scales))
+    return fail(RA_ERR_INVALID_ARG, "%s: per-token INT8 KV needs the k_scales and v_scales planes", fn);
+  if (!aligned16(a->qkv) || !aligned16(a->q_out) || !aligned16(a->rope_table) || !aligned16(a->k_cache) ||
+      !aligned16(a->v_cache) || (a->qkv_token_stride % 8) || (a->q_token_stride % 8) ||
+      (tok && (!aligned16(a->k_scales) || !aligned16(a->v_scales))))
+    return fail(RA_ERR_MISALIGNED, "%s: qkv, q_out, rope_table, the caches (and scale planes) must be 16-byte "
+                "aligned and token strides multiples of 8", fn);
+  const bool quant = per_layer_scales(a->kv_dtype);
+  ra::RopeLaunch L{a->qkv, a->src_dtype == RA_BF16, a->qkv_token_stride, a->num_tokens, a->positions,
+                   a->rope_table, a->max_position, a->rotary_dim, a->q_out, a->q_token_stride, a->slot_mapping,
+                   a->k_cache, a->v_cache, kv_kind(a->kv_dtype), a->num_pages, a->num_q_heads, a->num_kv_heads,
+                   a->head_dim, quant ? a->k_scale : 1.0f, quant ? a->v_scale : 1.0f, a->k_scales, a->v_scales};
+  const hipError_t e = ra::launch_qkv_rope(L, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(RA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return RA_OK;
 }
 

@@ -32,6 +32,33 @@ struct StoreLaunch {
 };
 hipError_t launch_kv_store(const StoreLaunch& a, hipStream_t s);
 
+// Packed QKV rows -> rotated Q, and rotated K + V quantised into the caches.
+struct RopeLaunch {
+  const void* qkv;       // [T][(hq + 2 hkv) * head_dim] fp16 / bf16
+  bool src_bf16;
+  int64_t qkv_stride;    // elements per token
+  int64_t num_tokens;
+  const int64_t* positions;
+  const float* table;    // [max_pos][2][rot / 2] fp32: cos, then sin
+  int64_t max_pos;
+  int rot;               // rotary dims, a multiple of 16, <= head_dim
+  void* q_out;           // [T][hq][head_dim], source dtype
+  int64_t q_stride;      // elements per token
+  const int64_t* slots;
+  void* k_cache;
+  void* v_cache;
+  int kv;                // KvKind
+  int64_t num_pages;
+  int hq;
+  int hkv;
+  int head_dim;
+  float k_scale;         // 1 unless per-layer E4M3 / INT8
+  float v_scale;
+  float* k_scales;       // KV_I8T scale planes
+  float* v_scales;
+};
+hipError_t launch_qkv_rope(const RopeLaunch& a, hipStream_t s);
+
 struct GatherLaunch {
   const void* cache;
   int which;             // 0 K, 1 V

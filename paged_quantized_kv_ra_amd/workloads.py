@@ -262,6 +262,22 @@ def build(name, seed, *, ctx, q_len, num_q_heads, num_kv_heads, head_dim,
         cache_sentinel=sentinel)
 
 
+def packed_qkv(seed, num_tokens, num_q_heads, num_kv_heads, head_dim, src_dtype="f16", row_pad=0):
+    """Rows of a fused QKV projection output: [T][(Hq + 2 Hkv) * D + row_pad]
+    N(0, 1) values in the source dtype (fp16, or bf16 bit patterns); the pad
+    columns make the row stride larger than the packed row."""
+    rng = np.random.default_rng(seed)
+    return _normal(rng, (num_tokens, (num_q_heads + 2 * num_kv_heads) * head_dim + row_pad), src_dtype)
+
+
+def step_positions_and_slots(w):
+    """Positions (ctx_b - q_len_b + i) and cache slots of a workload's new
+    tokens, in Q order."""
+    pos = np.concatenate([np.arange(int(w.ctx[b]) - int(w.q_len[b]), int(w.ctx[b]), dtype=np.int64)
+                          for b in range(w.batch)])
+    return pos, w.token_slots[w.new_token_rows()]
+
+
 # ---------------------------------------------------------------------------
 # The five benchmark workloads (seed = index - 1) and the sliding-window one.
 

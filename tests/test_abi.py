@@ -47,15 +47,17 @@ def test_exports_every_declared_symbol():
 
 def test_abi_version():
     L = _lib()
-    assert L.abi_version() == 2001
+    assert L.abi_version() == 3001
 
 
-def test_struct_layout_matches_c():
+@pytest.mark.parametrize("cname,pyname", [("ra_attn_args", "AttnArgs"), ("ra_qkv_rope_args", "RopeArgs")])
+def test_struct_layout_matches_c(cname, pyname):
     L = _lib()
-    fields = [f for f, _ in L.AttnArgs._fields_]
+    S = getattr(L, pyname)
+    fields = [f for f, _ in S._fields_]
     src = ['#include <stdio.h>', '#include <stddef.h>', '#include "ra_kv.h"', 'int main(void) {',
-           'printf("size %zu\\n", sizeof(ra_attn_args));']
-    src += [f'printf("{f} %zu\\n", offsetof(ra_attn_args, {f}));' for f in fields]
+           f'printf("size %zu\\n", sizeof({cname}));']
+    src += [f'printf("{f} %zu\\n", offsetof({cname}, {f}));' for f in fields]
     src += ["return 0; }"]
     with tempfile.TemporaryDirectory() as d:
         c = os.path.join(d, "t.c")
@@ -64,9 +66,9 @@ def test_struct_layout_matches_c():
         subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), c, "-o", exe],
                        check=True)
         got = dict(l.split() for l in subprocess.run([exe], capture_output=True, text=True).stdout.splitlines())
-    assert int(got["size"]) == ctypes.sizeof(L.AttnArgs)
+    assert int(got["size"]) == ctypes.sizeof(S)
     for f in fields:
-        assert int(got[f]) == getattr(L.AttnArgs, f).offset, f
+        assert int(got[f]) == getattr(S, f).offset, f
 
 
 def test_header_compiles_as_c_and_cpp():
@@ -318,3 +320,107 @@ def test_attn_int8_token_needs_aligned_planes_and_ignores_layer_scales():
     pl = ctypes.c_int64()
     a.k_scales = FAKE
     assert lib.ra_paged_attn_workspace(ctypes.byref(a), ctypes.byref(slots), ctypes.byref(po), ctypes.byref(pl)) == 0
+
+
+def _rope_args(L, **kw):
+    a = L.RopeArgs()
+    a.struct_size = ctypes.sizeof(L.RopeArgs)
+    a.qkv = FAKE
+    a.src_dtype = L.RA_F16
+    a.qkv_token_stride = (16 + 4) * 128
+    a.num_tokens = 8
+    a.positions = FAKE
+    a.rope_table = FAKE
+    a.max_position = 1024
+    a.rotary_dim = 128
+    a.q_out = FAKE
+    a.q_token_stride = 16 * 128
+    a.slot_mapping = FAKE
+    a.k_cache = FAKE
+    a.v_cache = FAKE
+    a.kv_dtype = L.RA_KV_FP8_E4M3
+    a.k_scale = 0.01
+    a.v_scale = 0.01
+    a.num_pages = 10
+    a.num_q_heads = 16
+    a.num_kv_heads = 2
+    a.head_dim = 128
+    a.page_size = 16
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+BAD_ROPE = [
+    (dict(struct_size=8), 1, "struct_size"),
+    (dict(num_tokens=-1), 1, "num_tokens"),
+    (dict(src_dtype=3), 2, "src_dtype"),
+    (dict(kv_dtype=7), 2, "kv_dtype"),
+    (dict(head_dim=96), 2, "head_dim"),
+    (dict(page_size=8), 2, "page_size"),
+    (dict(num_kv_heads=0), 1, "num_kv_heads"),
+    (dict(num_pages=0), 1, "num_pages"),
+    (dict(rotary_dim=24), 1, "rotary_dim"),
+    (dict(rotary_dim=256), 1, "rotary_dim"),
+    (dict(max_position=0), 1, "max_position"),
+    (dict(k_scale=0.0), 1, "no fallback"),
+    (dict(v_scale=float("inf")), 1, "no fallback"),
+    (dict(qkv_token_stride=16 * 128), 1, "qkv_token_stride"),
+    (dict(q_token_stride=8), 1, "q_token_stride"),
+    (dict(num_tokens=1 << 30), 1, "chunks"),
+    (dict(positions=None), 1, "non-NULL"),
+    (dict(rope_table=None), 1, "non-NULL"),
+    (dict(kv_dtype=4), 1, "planes"),
+    (dict(q_out=FAKE + 8), 3, "aligned"),
+    (dict(qkv_token_stride=(16 + 4) * 128 + 4), 3, "aligned"),
+]
+
+
+@pytest.mark.parametrize("kw,status,msg", BAD_ROPE, ids=[f"{i}-{m}" for i, (_, _, m) in enumerate(BAD_ROPE)])
+def test_qkv_rope_validation(kw, status, msg):
+    L = _lib()
+    lib = L.load_library()
+    st = lib.ra_qkv_rope_store(ctypes.byref(_rope_args(L, **kw)), None)
+    assert st == status, (st, lib.ra_last_error())
+    assert msg in lib.ra_last_error().decode()
+
+
+def test_qkv_rope_zero_tokens_and_fp16_ignores_scales():
+    L = _lib()
+    lib = L.load_library()
+    assert lib.ra_qkv_rope_store(ctypes.byref(_rope_args(L, num_tokens=0, qkv=None, positions=None)), None) == 0
+    a = _rope_args(L, num_tokens=0, kv_dtype=L.RA_KV_F16, k_scale=float("nan"), v_scale=-1.0)
+    assert lib.ra_qkv_rope_store(ctypes.byref(a), None) == 0
+
+
+@pytest.mark.parametrize("max_pos,rot,base,factor,orig", [
+    (4096, 128, 10000.0, 1.0, 0),            # plain RoPE
+    (4096, 128, 1e6, 2.0, 1024),             # YaRN over a ramp of dims
+    (600, 64, 10000.0, 4.0, 256),
+    (300, 16, 500.0, 2.0, 100),
+])
+def test_rope_table_matches_oracle(max_pos, rot, base, factor, orig):
+    """The library's host table against the oracle's fp64 table rounded to
+    fp32: equal up to one fp32 rounding step (the two round from separately
+    computed fp64 values)."""
+    import numpy as np
+    from oracle import rope as R
+    L = _lib()
+    got = L.rope_table(max_pos, rot, base, factor, orig, device=None).numpy()
+    want = R.rope_table(max_pos, rot, base, factor, original_max=orig or None)
+    assert got.shape == want.shape
+    ulp = np.spacing(np.abs(want).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(got.astype(np.float64) - want) <= ulp + 1e-300)
+    assert np.mean(got == want.astype(np.float32)) > 0.999
+
+
+def test_rope_table_validation():
+    L = _lib()
+    lib = L.load_library()
+    buf = (ctypes.c_float * 64)()
+    assert lib.ra_rope_table(buf, 4, 15, 10000.0, 1.0, 0, 32.0, 1.0) == 1
+    assert lib.ra_rope_table(buf, 0, 16, 10000.0, 1.0, 0, 32.0, 1.0) == 1
+    assert lib.ra_rope_table(buf, 4, 16, 1.0, 1.0, 0, 32.0, 1.0) == 1
+    assert lib.ra_rope_table(buf, 4, 16, 10000.0, 2.0, 0, 32.0, 1.0) == 1
+    assert lib.ra_rope_table(None, 4, 16, 10000.0, 1.0, 0, 32.0, 1.0) == 1
+    assert lib.ra_rope_table(buf, 4, 16, 10000.0, 2.0, 64, 32.0, 1.0) == 0
