@@ -12,7 +12,8 @@
 // Per wavefront and 16-token page, for each 16-row tile of query rows:
 //   S^T[16 keys][16 rows] = K[16][D] . Q^T[D][16]      v_mfma_f32_16x16x32_f16 (D/32 steps)
 //   P^T = exp2(c * S^T - c * m)                       online softmax, fp32, rescaled lazily
-//   O^T[D][16 rows]      += V^T[D][16] . P^T[16][16]   v_mfma_f32_16x16x16_f16 (D/16 tiles)
+// and per pair of pages (32 keys; a lone last page uses the 16x16x16 form):
+//   O^T[D][16 rows]      += V^T[D][32] . P^T[32][16]   v_mfma_f32_16x16x32_f16 (D/16 tiles)
 // The cache layout puts every lane's 16-byte piece of a page directly in the
 // operand order of both products: a K lane holds one token's contiguous D/4
 // dims, a V lane holds four consecutive tokens of D/16 dims, and the S^T
@@ -181,16 +182,16 @@ __device__ __forceinline__ f16x8 k_operand(const PageRegs<KV, D>& r, int ks) {
 
 // V operand of dim tile mt: tokens 4 kgrp .. 4 kgrp + 3 of the lane's dim.
 template <int KV, int D>
-__device__ __forceinline__ f16x4 v_operand(const PageRegs<KV, D>& r, int mt) {
+__device__ __forceinline__ f16x4 v_operand(const u32x4 (&v)[Geo<KV, D>::SLABS], int mt) {
   if constexpr (KV == KV_F16) {
-    const u32x4 w = r.v[mt >> 1];
+    const u32x4 w = v[mt >> 1];
     const uint32_t a = (mt & 1) ? w[2] : w[0];
     const uint32_t b = (mt & 1) ? w[3] : w[1];
     const f16x2 lo = as<f16x2>(a);
     const f16x2 hi = as<f16x2>(b);
     return f16x4{lo[0], lo[1], hi[0], hi[1]};
   } else {
-    const u32x4 w = r.v[mt >> 2];
+    const u32x4 w = v[mt >> 2];
     return codes4_to_f16x4<KV>(w[mt & 3]);
   }
 }
@@ -199,15 +200,20 @@ template <int KV, int D, int NT>
 struct Acc {
   f32x4 o[Geo<KV, D>::MT][NT];
   float m[NT];
+  float mc[NT];   // c * m, or 0 while m = -inf: the rows' exponent offset
   float l[NT];
 };
 
+// QK, masks and the online softmax of one page.  p receives the page's
+// unnormalised probabilities (times the per-token V scales for per-token
+// INT8); a refresh of the running max also rescales `pend`, the
+// probabilities of an earlier page whose PV product is still to come.
 template <int KV, int D, int NT>
-__device__ __forceinline__ void compute_page(Acc<KV, D, NT>& acc, PageRegs<KV, D>& r,
-                                             const f16x8 (&qf)[NT][Geo<KV, D>::KS],
-                                             const AttnLaunch& a, const UnitPages& pg, int32_t n, int32_t ctx,
-                                             const SeqFrame& fr, const int32_t (&pos)[NT], int kgrp, float c,
-                                             float thr) {
+__device__ __forceinline__ void scores_softmax(Acc<KV, D, NT>& acc, PageRegs<KV, D>& r,
+                                               const f16x8 (&qf)[NT][Geo<KV, D>::KS],
+                                               const AttnLaunch& a, const UnitPages& pg, int32_t n, int32_t ctx,
+                                               const SeqFrame& fr, const int32_t (&pos)[NT], int kgrp, float c,
+                                               float thr, float (&p)[NT][4], float (&pend)[NT][4]) {
   using G = Geo<KV, D>;
   // ---- scores S^T for the page's 16 keys
   f32x4 s[NT];
@@ -267,31 +273,71 @@ __device__ __forceinline__ void compute_page(Acc<KV, D, NT>& acc, PageRegs<KV, D
       const float alpha = upd ? (acc.m[nt] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((acc.m[nt] - rm) * c))
                               : 1.0f;
       acc.m[nt] = upd ? rm : acc.m[nt];
+      acc.mc[nt] = acc.m[nt] == -INFINITY ? 0.0f : acc.m[nt] * c;
       acc.l[nt] *= alpha;
 #pragma unroll
       for (int mt = 0; mt < G::MT; ++mt) acc.o[mt][nt] *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pend[nt][i] *= alpha;
     }
   }
-  f16x4 pf[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const float mc = acc.m[nt] == -INFINITY ? 0.0f : acc.m[nt] * c;
     float ps = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float e = __builtin_amdgcn_exp2f(fmaf(s[nt][i], c, -mc));
+      const float e = __builtin_amdgcn_exp2f(fmaf(s[nt][i], c, -acc.mc[nt]));
       ps += e;
-      pf[nt][i] = KV == KV_I8T ? (f16)(e * r.vs[i]) : (f16)e;   // per-token V scales ride on P
+      p[nt][i] = KV == KV_I8T ? e * r.vs[i] : e;   // per-token V scales ride on P
     }
     acc.l[nt] += ps;
   }
-  // ---- O^T += V^T . P^T
+}
+
+// O^T += V^T . P^T for one page (16 keys): D/16 x NT 16x16x16 products.
+template <int KV, int D, int NT>
+__device__ __forceinline__ void pv_single(Acc<KV, D, NT>& acc, const u32x4 (&v)[Geo<KV, D>::SLABS],
+                                          const float (&p)[NT][4]) {
+  using G = Geo<KV, D>;
+  f16x4 pf[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pf[nt][i] = (f16)p[nt][i];
 #pragma unroll
   for (int mt = 0; mt < G::MT; ++mt) {
-    const f16x4 vop = v_operand<KV, D>(r, mt);
+    const f16x4 vop = v_operand<KV, D>(v, mt);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
       acc.o[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(vop, pf[nt], acc.o[mt][nt], 0, 0, 0);
+  }
+}
+
+// O^T += V^T . P^T for two pages at once with the 16x16x32 product (twice the
+// 16x16x16 rate): the contraction runs over 32 keys, the lane's k-slots 0-3
+// holding its 4 keys of page A and slots 4-7 the same keys of page B, in the
+// V operand and the P operand alike.
+template <int KV, int D, int NT>
+__device__ __forceinline__ void pv_pair(Acc<KV, D, NT>& acc, const u32x4 (&va)[Geo<KV, D>::SLABS],
+                                        const float (&pa)[NT][4], const u32x4 (&vb)[Geo<KV, D>::SLABS],
+                                        const float (&pb)[NT][4]) {
+  using G = Geo<KV, D>;
+  f16x8 pf[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pf[nt][i] = (f16)pa[nt][i];
+      pf[nt][4 + i] = (f16)pb[nt][i];
+    }
+#pragma unroll
+  for (int mt = 0; mt < G::MT; ++mt) {
+    const f16x4 x = v_operand<KV, D>(va, mt);
+    const f16x4 y = v_operand<KV, D>(vb, mt);
+    const f16x8 vop = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      acc.o[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pf[nt], acc.o[mt][nt], 0, 0, 0);
   }
 }
 
@@ -404,6 +450,7 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a,
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     acc.m[nt] = -INFINITY;
+    acc.mc[nt] = 0.0f;
     acc.l[nt] = 0.0f;
 #pragma unroll
     for (int mt = 0; mt < G::MT; ++mt) acc.o[mt][nt] = f32x4{0, 0, 0, 0};
@@ -421,6 +468,18 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a,
     uint8_t (*ring)[kSlab] = &sm_raw[wave * NR * G::NSL];
     float* scl = &sm_scl[KV == KV_I8T ? wave * NR * 32 : 0];
     IdRing ids{sm_id[0][lane], 0};
+    // pages are taken in pairs for the PV product: the even page of a pair
+    // waits (its masked V codes and probabilities in registers) for the odd
+    // one; an odd count leaves the last page to a single-page product
+    static_assert(NR % 2 == 0, "page pairs must not straddle ring rounds");
+    u32x4 pend_v[G::SLABS];
+    float pend_p[NT][4];
+#pragma unroll
+    for (int sl = 0; sl < G::SLABS; ++sl) pend_v[sl] = u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pend_p[nt][i] = 0.0f;
 #pragma unroll
     for (int j = 0; j < NR; ++j)
       if (j < my_pages)
@@ -438,7 +497,18 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a,
             wait_vmcnt<0>();
           PageRegs<KV, D> r;
           read_page<KV, D>(r, ring + j * G::NSL, scl + j * 32, lane_off, kgrp);
-          compute_page<KV, D, NT>(acc, r, qf, a, pg, ws.page(k), ctx, frg, pos, kgrp, c, thr);
+          float p[NT][4];
+          scores_softmax<KV, D, NT>(acc, r, qf, a, pg, ws.page(k), ctx, frg, pos, kgrp, c, thr, p, pend_p);
+          if (j & 1) {   // k odd (the ring depth is even): the pair is complete
+            pv_pair<KV, D, NT>(acc, pend_v, pend_p, r.v, p);
+          } else {
+#pragma unroll
+            for (int sl = 0; sl < G::SLABS; ++sl) pend_v[sl] = r.v[sl];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) pend_p[nt][i] = p[nt][i];
+          }
           // the slot's reads have returned (their values were consumed) before
           // the next load may overwrite it
           wait_lgkmcnt0();
@@ -448,6 +518,7 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a,
         }
       }
     }
+    if (my_pages & 1) pv_single<KV, D, NT>(acc, pend_v, pend_p);
   }
   wait_vmcnt<0>();   // no ring load may land after the ring becomes the merge buffer
 
