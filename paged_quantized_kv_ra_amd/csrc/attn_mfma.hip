@@ -196,12 +196,19 @@ __device__ __forceinline__ f16x4 v_operand(const u32x4 (&v)[Geo<KV, D>::SLABS], 
   }
 }
 
+// Row sums of P ride on the matrix cores as one more PV tile whose V operand
+// is all ones (every lane of that tile then holds its row's whole sum), except
+// for per-token INT8, whose P carries the V scales and is summed on the VALU.
+template <int KV>
+constexpr bool kOnesSum = KV != KV_I8T;
+
 template <int KV, int D, int NT>
 struct Acc {
   f32x4 o[Geo<KV, D>::MT][NT];
+  f32x4 ls[NT];   // row sums by the ones tile
   float m[NT];
   float mc[NT];   // c * m, or 0 while m = -inf: the rows' exponent offset
-  float l[NT];
+  float l[NT];    // the lane's partial row sums (per-token INT8)
 };
 
 // QK, masks and the online softmax of one page.  p receives the page's
@@ -233,6 +240,47 @@ __device__ __forceinline__ void scores_softmax(Acc<KV, D, NT>& acc, PageRegs<KV,
   // ---- masks (only on pages that can hold an invisible key).  Keys past ctx
   // (stale bytes of the last page) also get their V codes zeroed so that
   // 0 * garbage cannot produce NaN.
+  // ---- online softmax with lazy max refresh
+  const auto softmax = [&]() {
+    float mx[NT];
+    bool trig = false;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      mx[nt] = __builtin_elementwise_maximum(__builtin_elementwise_maximum(s[nt][0], s[nt][1]),
+                                             __builtin_elementwise_maximum(s[nt][2], s[nt][3]));
+      trig |= mx[nt] > acc.m[nt] + thr;
+    }
+    if (__any(trig)) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float rm = mx[nt];
+        rm = __builtin_elementwise_maximum(rm, __shfl_xor(rm, 16));
+        rm = __builtin_elementwise_maximum(rm, __shfl_xor(rm, 32));
+        const bool upd = rm > acc.m[nt] + thr;
+        const float alpha =
+            upd ? (acc.m[nt] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((acc.m[nt] - rm) * c)) : 1.0f;
+        acc.m[nt] = upd ? rm : acc.m[nt];
+        acc.mc[nt] = acc.m[nt] == -INFINITY ? 0.0f : acc.m[nt] * c;
+        if constexpr (kOnesSum<KV>) acc.ls[nt] *= alpha;
+        else acc.l[nt] *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt) acc.o[mt][nt] *= alpha;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pend[nt][i] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float ps = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(s[nt][i], c, -acc.mc[nt]));
+        if constexpr (!kOnesSum<KV>) ps += e;
+        p[nt][i] = KV == KV_I8T ? e * r.vs[i] : e;   // per-token V scales ride on P
+      }
+      if constexpr (!kOnesSum<KV>) acc.l[nt] += ps;
+    }
+  };
   const int32_t tok0 = pg.page(n) * kPage;
   const bool need_mask = (tok0 + kPage - 1 > fr.pmin) || (tok0 + kPage - 1 >= ctx) ||
                          (a.window >= 0 && tok0 <= fr.pmax - a.window);
@@ -255,43 +303,7 @@ __device__ __forceinline__ void scores_softmax(Acc<KV, D, NT>& acc, PageRegs<KV,
 #pragma unroll
       for (int w = 0; w < 4; ++w) r.v[sl][w] &= KV == KV_F16 ? ((w & 1) ? keep_hi : keep_lo) : keep8;
   }
-  // ---- online softmax with lazy max refresh
-  float mx[NT];
-  bool trig = false;
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    mx[nt] = fmaxf(fmaxf(s[nt][0], s[nt][1]), fmaxf(s[nt][2], s[nt][3]));
-    trig |= mx[nt] > acc.m[nt] + thr;
-  }
-  if (__any(trig)) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float rm = mx[nt];
-      rm = fmaxf(rm, __shfl_xor(rm, 16));
-      rm = fmaxf(rm, __shfl_xor(rm, 32));
-      const bool upd = rm > acc.m[nt] + thr;
-      const float alpha = upd ? (acc.m[nt] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((acc.m[nt] - rm) * c))
-                              : 1.0f;
-      acc.m[nt] = upd ? rm : acc.m[nt];
-      acc.mc[nt] = acc.m[nt] == -INFINITY ? 0.0f : acc.m[nt] * c;
-      acc.l[nt] *= alpha;
-#pragma unroll
-      for (int mt = 0; mt < G::MT; ++mt) acc.o[mt][nt] *= alpha;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pend[nt][i] *= alpha;
-    }
-  }
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    float ps = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float e = __builtin_amdgcn_exp2f(fmaf(s[nt][i], c, -acc.mc[nt]));
-      ps += e;
-      p[nt][i] = KV == KV_I8T ? e * r.vs[i] : e;   // per-token V scales ride on P
-    }
-    acc.l[nt] += ps;
-  }
+  softmax();
 }
 
 // O^T += V^T . P^T for one page (16 keys): D/16 x NT 16x16x16 products.
@@ -310,6 +322,11 @@ __device__ __forceinline__ void pv_single(Acc<KV, D, NT>& acc, const u32x4 (&v)[
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
       acc.o[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(vop, pf[nt], acc.o[mt][nt], 0, 0, 0);
+  }
+  if constexpr (kOnesSum<KV>) {
+    const f16x4 ones = {(f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f};
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc.ls[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, pf[nt], acc.ls[nt], 0, 0, 0);
   }
 }
 
@@ -339,10 +356,21 @@ __device__ __forceinline__ void pv_pair(Acc<KV, D, NT>& acc, const u32x4 (&va)[G
     for (int nt = 0; nt < NT; ++nt)
       acc.o[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pf[nt], acc.o[mt][nt], 0, 0, 0);
   }
+  if constexpr (kOnesSum<KV>) {
+    const f16x8 ones = {(f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f};
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc.ls[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf[nt], acc.ls[nt], 0, 0, 0);
+  }
 }
 
+// A decode tile (NT = 1) whose page ring takes at most 8 KiB per wave keeps
+// to 128 VGPRs, so that two workgroups share a CU.
 template <int KV, int D, int NT>
-__global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
+constexpr int kWavesPerSimd = (NT == 1 && Geo<KV, D>::NRING * Geo<KV, D>::NSL <= 8) ? 4 : 2;
+
+template <int KV, int D, int NT>
+__global__ void __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<KV, D, NT>)))
+attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
   using G = Geo<KV, D>;
   // LDS: the per-wave page rings, reused for the cross-wave merge of O
   constexpr int kRingBytes = kWaves * G::NRING * G::NSL * kSlab;
@@ -452,6 +480,7 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a,
     acc.m[nt] = -INFINITY;
     acc.mc[nt] = 0.0f;
     acc.l[nt] = 0.0f;
+    acc.ls[nt] = f32x4{0, 0, 0, 0};
 #pragma unroll
     for (int mt = 0; mt < G::MT; ++mt) acc.o[mt][nt] = f32x4{0, 0, 0, 0};
   }
@@ -526,9 +555,14 @@ __global__ void __launch_bounds__(kWaves * kWave) attn_mfma_kernel(AttnLaunch a,
   // bad flag, then rescales its O to the common row maximum.
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    float l = acc.l[nt];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    float l;
+    if constexpr (kOnesSum<KV>) {
+      l = acc.ls[nt][0];   // the whole row's sum in every lane of the row
+    } else {
+      l = acc.l[nt];
+      l += __shfl_xor(l, 16);
+      l += __shfl_xor(l, 32);
+    }
     if (kgrp == 0) {
       reinterpret_cast<float*>(&sm_ml[0][nt * 16 + ncol][0])[wave] = acc.m[nt];
       reinterpret_cast<float*>(&sm_ml[1][nt * 16 + ncol][0])[wave] = l;
