@@ -217,11 +217,13 @@ def algorithmic_bytes(w):
     """HBM bytes one attention launch must move: the visible KV tokens' codes
     (2 * Hkv * D * e per token, plus 2 * Hkv * 4 B of scales for per-token
     INT8), the block-table entries of the visited pages
-    (4 B per 16 tokens per sequence) and the queries."""
+    (4 B per 16 tokens per sequence), the queries read and the output and
+    its lse written (partials are the implementation's own traffic)."""
     kv = w.kv_bytes_attended()
     bt = 4 * sum(-(-int(c) // 16) for c in w.ctx)
     q = w.q.nbytes
-    return kv + bt + q
+    out = w.q.nbytes + 4 * w.total_q * w.num_q_heads
+    return kv + bt + q + out
 
 
 def cpu_baseline(w, seconds):
