@@ -1,9 +1,12 @@
 #!/usr/bin/env python3
 """Benchmark of one decode/verify step of paged, quantized-KV attention on one MI355X.
 
-A step is the whole hot path over one batch: ra_kv_store of the step's new
-K/V rows (the 1 + 4 verify tokens of every sequence), ra_paged_attn over the
-paged cache (partials per KV partition) and ra_lse_merge.  Inputs are seeded
+A step is the whole hot path over one batch: the store of the step's new K/V
+rows (the 1 + 4 verify tokens of every sequence), ra_paged_attn over the
+paged cache (partials per KV partition) and ra_lse_merge.  Decode and verify
+blocks store their new tokens inside the attention launch (the fused store of
+ra_attn_args); prefill blocks, and --separate-store, use a ra_kv_store launch
+first.  Inputs are seeded
 synthetic data already resident in HBM.  Each step uses the next of L
 identical copies of the KV pool (at least 1 GiB in total), the way successive
 layers of a model read distinct caches, so the 256 MB Infinity Cache cannot
@@ -63,6 +66,9 @@ def parse():
     ap.add_argument("--fused-qkv", action="store_true",
                     help="store the new tokens with ra_qkv_rope_store (packed QKV rows, RoPE with YaRN "
                          "factor 2, Q written for attention) instead of ra_kv_store")
+    ap.add_argument("--separate-store", action="store_true",
+                    help="store the new tokens with a ra_kv_store launch before the attention instead of the "
+                         "attention launch's fused store")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from the host instead of replaying captured HIP graphs")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -87,7 +93,7 @@ def copy_calibration():
 class Step:
     """Device state and prebuilt C-ABI argument blocks for one workload."""
 
-    def __init__(self, w, fused_qkv=False):
+    def __init__(self, w, fused_qkv=False, separate_store=False):
         import torch
         import paged_quantized_kv_ra_amd as P
         from paged_quantized_kv_ra_amd import _lib as L
@@ -127,11 +133,20 @@ class Step:
         T, hq = self.q.shape[0], self.q.shape[1]
         self.out = torch.empty_like(self.q)
         self.lse = torch.empty((T, hq), dtype=torch.float32, device=dev)
+        # decode and verify blocks (at most 48 rows per KV head) store their new
+        # tokens inside the attention launch; prefill blocks, --separate-store
+        # and --fused-qkv store them with a launch of their own first
+        g = w.num_q_heads // hkv
+        self.store_mode = ("qkv_rope_store" if fused_qkv else
+                           "kv_store" if separate_store or g * w.max_q_len > 48 else "fused")
+        fused = self.store_mode == "fused"
         self.args = []
         for k, v, ks, vs in self.pools:
             a = L._attn_args(self.q, k, v, self.bt, self.ctx, self.qsl, w.kv_dtype, w.k_scale, w.v_scale,
                              w.softmax_scale, w.max_q_len, int(w.q_len.min()), w.max_context_len,
-                             w.window_left, w.num_sinks, w.num_splits, hkv, ks, vs)
+                             w.window_left, w.num_sinks, w.num_splits, hkv, ks, vs,
+                             new_k=self.k_new if fused else None, new_v=self.v_new if fused else None,
+                             new_slots=self.slots_new if fused else None)
             self.args.append(a)
         self.slots, po_n, _ = L.paged_attn_workspace(self.args[0])
         # one partition slot (a long prefill chunk): the kernel writes out and
@@ -189,7 +204,9 @@ class Step:
         w, lib, L = self.w, self.lib, self.L
         k, v, ks, vs = self.pools[i % self.copies]
         s = ctypes.c_void_p(stream)
-        if self.rope_args is not None:
+        if self.store_mode == "fused":
+            st = 0                   # the attention launch stores the new tokens itself
+        elif self.rope_args is not None:
             st = lib.ra_qkv_rope_store(ctypes.byref(self.rope_args[i % self.copies]), s)
         elif ks is not None:
             st = lib.ra_kv_store_int8_token(self.k_new.data_ptr(), self.v_new.data_ptr(), L.RA_F16,
@@ -397,7 +414,7 @@ def main():
     t0 = time.time()
     w = make()
     log(f"built {w.name} in {time.time() - t0:.1f}s")
-    step = Step(w, fused_qkv=args.fused_qkv)
+    step = Step(w, fused_qkv=args.fused_qkv, separate_store=args.separate_store)
     log(f"pool copies: {step.copies}, partition slots: {step.slots}")
     if args.eager:
         ms_per_step, attn_avg_ms, wall = time_eager(step, args, torch)
@@ -444,7 +461,7 @@ def main():
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "kv_dtype": w.kv_dtype, "page_size": 16, "partition_slots": step.slots,
                    "kv_pool_copies": step.copies, "launch": "eager" if args.eager else "hip_graph",
-                   "store": "qkv_rope_store" if args.fused_qkv else "kv_store",
+                   "store": step.store_mode,
                    "parallelism": "single GPU"},
         "roofline": roof,
         "attended_tokens_per_step": tokens,

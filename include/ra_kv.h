@@ -88,7 +88,7 @@
 extern "C" {
 #endif
 
-#define RA_KV_ABI_VERSION 3
+#define RA_KV_ABI_VERSION 4
 #define RA_KV_LAYOUT_ID 1
 #define RA_KV_PAGE_SIZE 16
 #define RA_KV_MAX_SPLITS 4096
@@ -234,7 +234,7 @@ int32_t ra_qkv_rope_store(const ra_qkv_rope_args* args, void* stream);
  *
  * For sequence b: q_len_b = query_start_loc[b+1] - query_start_loc[b] and
  * ctx_b = context_lens[b], which INCLUDES this step's q_len_b tokens (store
- * them first).  Query i of the block sits at position pos = ctx_b - q_len_b + i;
+ * them first, or pass them for the fused store below).  Query i of the block sits at position pos = ctx_b - q_len_b + i;
  * query head h reads KV head h / (num_q_heads / num_kv_heads).  Key j is
  * visible iff j <= pos and (window_left < 0 or pos - j < window_left or
  * j < num_sinks).  out = softmax(softmax_scale * q . k) v over visible keys,
@@ -263,6 +263,20 @@ int32_t ra_qkv_rope_store(const ra_qkv_rope_args* args, void* stream);
  *     chunk is attended in one pass).
  * The grid's slot count follows from max_context_len, max_q_len and
  * min_q_len; a sequence whose q_len_b is below min_q_len is written as NaN.
+ *
+ * Fused store: with new_k non-NULL the launch first does what ra_kv_store
+ * would do with new_k / new_v / new_slots for the query tokens (row q of
+ * new_k and new_v is the K and V of query token q, slot new_slots[q]; slot
+ * < 0 or >= num_pages * 16 stores nothing), each token stored by the
+ * workgroups of the partition holding its position, before they read it; the
+ * separate ra_kv_store call and its launch go away.  The slot of query i of
+ * sequence b must be the block table's slot for its position p (local to this
+ * cache): block_tables[b][p / 16] * 16 + p % 16.  Tokens whose position lies
+ * outside [0, ctx_b) are not stored (they belong to another context-parallel
+ * shard).  Supported for decode and verify blocks, (Hq / Hkv) * max_q_len <=
+ * 48; longer blocks (prefill) return RA_ERR_UNSUPPORTED and are stored with
+ * ra_kv_store first.  The store's format, scales and rounding are those of
+ * ra_kv_store (per-token INT8 writes its scale planes too).
  * With more than
  * one partition slot the kernel writes partial_out [slots][total_q][Hq][D] and
  * partial_lse [slots][total_q][Hq] (fp32; out already normalised; an empty
@@ -306,6 +320,14 @@ typedef struct ra_attn_args {
   const float* v_scales;           /* above); ignored by the other formats       */
   const int32_t* kv_pos0;          /* [batch] or NULL: global position of key 0  */
   const int32_t* q_pos0;           /* [batch] or NULL: global position of query 0*/
+  /* Fused store (decode and verify): the query tokens' own K/V rows, stored
+     by the launch itself before it reads them; new_k = NULL stores nothing. */
+  const void* new_k;               /* [total_q][num_kv_heads][head_dim] or NULL  */
+  const void* new_v;
+  int32_t new_dtype;               /* RA_F16 or RA_BF16                          */
+  int64_t new_k_stride;            /* elements between tokens, multiple of 8     */
+  int64_t new_v_stride;
+  const int64_t* new_slots;        /* [total_q] cache slot of each query token   */
 } ra_attn_args;
 
 /*

@@ -66,6 +66,12 @@ class AttnArgs(_c.Structure):
         ("v_scales", _vp),
         ("kv_pos0", _vp),
         ("q_pos0", _vp),
+        ("new_k", _vp),
+        ("new_v", _vp),
+        ("new_dtype", _c.c_int32),
+        ("new_k_stride", _c.c_int64),
+        ("new_v_stride", _c.c_int64),
+        ("new_slots", _vp),
     ]
 
 
@@ -212,7 +218,8 @@ def kv_store(k, v, slot_mapping, k_cache, v_cache, kv_dtype, k_scale=1.0, v_scal
 
 def _attn_args(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, kv_dtype, k_scale,
                v_scale, softmax_scale, max_q_len, min_q_len, max_context_len, window_left, num_sinks,
-               num_splits, num_kv_heads, k_scales=None, v_scales=None, kv_pos0=None, q_pos0=None):
+               num_splits, num_kv_heads, k_scales=None, v_scales=None, kv_pos0=None, q_pos0=None, new_k=None,
+               new_v=None, new_slots=None):
     T, hq, D = q.shape
     a = AttnArgs()
     a.struct_size = _c.sizeof(AttnArgs)
@@ -245,6 +252,15 @@ def _attn_args(q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
     a.v_scales = None if v_scales is None else v_scales.data_ptr()
     a.kv_pos0 = None if kv_pos0 is None else kv_pos0.data_ptr()
     a.q_pos0 = None if q_pos0 is None else q_pos0.data_ptr()
+    if new_k is not None:            # fused store of the query tokens' K/V
+        assert new_v is not None and new_slots is not None and new_slots.dtype == torch.int64
+        assert new_k.stride(-1) == 1 and new_v.stride(-1) == 1 and new_k.dtype == new_v.dtype
+        a.new_k = new_k.data_ptr()
+        a.new_v = new_v.data_ptr()
+        a.new_dtype = _src_code(new_k)
+        a.new_k_stride = new_k.stride(0)
+        a.new_v_stride = new_v.stride(0)
+        a.new_slots = new_slots.data_ptr()
     return a
 
 
@@ -259,19 +275,22 @@ def paged_attn_workspace(args):
 def paged_attn(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, *, kv_dtype,
                max_q_len, max_context_len, k_scale=1.0, v_scale=1.0, softmax_scale=None, min_q_len=0,
                window_left=-1, num_sinks=0, num_splits=0, out=None, lse=None, partials_only=False,
-               workspace=None, stream=None, k_scales=None, v_scales=None, kv_pos0=None, q_pos0=None):
+               workspace=None, stream=None, k_scales=None, v_scales=None, kv_pos0=None, q_pos0=None,
+               new_k=None, new_v=None, new_slots=None):
     """Attention of the query blocks over the paged caches.
 
     q [total_q][Hq][D] fp16/bf16; block_tables int32 [B][stride];
     context_lens int32 [B]; query_start_loc int32 [B+1].  max_q_len and
     max_context_len are host upper bounds.  Returns (out, lse), or with
     partials_only=True (partial_out [S][total_q][Hq][D], partial_lse [S][total_q][Hq]).
+    new_k, new_v [total_q][Hkv][D] and new_slots int64 [total_q]: the query
+    tokens' own K/V, stored by the launch itself (decode and verify blocks).
     """
     T, hq, D = q.shape
     hkv = k_cache.shape[1]
     a = _attn_args(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, kv_dtype, k_scale,
                    v_scale, softmax_scale, max_q_len, min_q_len, max_context_len, window_left, num_sinks,
-                   num_splits, hkv, k_scales, v_scales, kv_pos0, q_pos0)
+                   num_splits, hkv, k_scales, v_scales, kv_pos0, q_pos0, new_k, new_v, new_slots)
     if not partials_only:
         if out is None:
             out = torch.empty_like(q)

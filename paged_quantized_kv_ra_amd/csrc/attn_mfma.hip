@@ -306,6 +306,53 @@ __device__ __forceinline__ void scores_softmax(Acc<KV, D, NT>& acc, PageRegs<KV,
   softmax();
 }
 
+// Fused store: quantise the unit's head's K and V rows of the query tokens
+// whose (local) positions fall in the partition [lo, hi) and write them at
+// their slots exactly as the KV store kernel does, before any page of the
+// partition is read.  32 threads per token for D = 128 (16 for K, 16 for V,
+// 8 dims each).  Returns whether anything was stored (workgroup-uniform).
+template <int KV, int D>
+__device__ __forceinline__ bool store_new_tokens(const AttnLaunch& a, int h, int32_t q0, int32_t q_len,
+                                                 int32_t pmin, int32_t lo, int32_t hi) {
+  constexpr int CH = D / 8;         // lanes per row
+  constexpr int E = KV == KV_F16 ? 2 : 1;
+  const int32_t i0 = max(0, lo - pmin), i1 = min(q_len, hi - pmin);
+  if (i0 >= i1) return false;
+  const int t = threadIdx.x;
+  const int c = t % CH;
+  const bool is_v = (t / CH) & 1;
+  const int64_t limit = a.num_pages * kPage;
+  for (int32_t base = i0; base < i1; base += kWaves * kWave / (2 * CH)) {
+    const int32_t i = base + t / (2 * CH);
+    if (i < i1) {   // whole rows of lanes are in or out
+      const int64_t row = q0 + i;
+      const uint16_t* src = reinterpret_cast<const uint16_t*>(is_v ? a.new_v : a.new_k) +
+                            row * (is_v ? a.new_v_stride : a.new_k_stride) + (int64_t)h * D + 8 * c;
+      const u32x4 raw = load16(src);
+      const int64_t slot = a.new_slots[row];
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint16_t b = (uint16_t)(raw[j >> 1] >> (16 * (j & 1)));
+        x[j] = a.new_bf16 ? bf16_to_f32(b) : (float)as<f16>(b);
+      }
+      float sc = is_v ? a.v_scale : a.k_scale;
+      if constexpr (KV == KV_I8T) sc = row_absmax(x, CH) / 127.0f;   // correctly rounded division
+      if (slot >= 0 && slot < limit) {
+        const int64_t page = slot >> 4;
+        const int tp = (int)(slot & 15);
+        if constexpr (KV == KV_I8T) {
+          if (c == 0) const_cast<float*>(is_v ? a.v_scales : a.k_scales)[(page * a.hkv + h) * kPage + tp] = sc;
+        }
+        // the caches and scale planes are the caller's writable buffers (read-only to the attention itself)
+        uint8_t* blk = const_cast<uint8_t*>(is_v ? a.v_cache : a.k_cache) + (page * a.hkv + h) * (int64_t)(kPage * D * E);
+        store_row8<KV, D>(blk, tp, 8 * c, x, sc, is_v);
+      }
+    }
+  }
+  return true;
+}
+
 // O^T += V^T . P^T for one page (16 keys): D/16 x NT 16x16x16 products.
 template <int KV, int D, int NT>
 __device__ __forceinline__ void pv_single(Acc<KV, D, NT>& acc, const u32x4 (&v)[Geo<KV, D>::SLABS],
@@ -455,7 +502,11 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
 #pragma unroll
     for (int ks = 0; ks < G::KS; ++ks) qraw[nt][ks] = load16(qp + 8 * ks);
   }
-  wait_vmcnt<0>();   // the first id chunks and the query rows have landed
+  // the fused store of the query tokens' own K/V (decode and verify blocks)
+  bool stored = false;
+  if (a.new_k != nullptr && !bad) stored = store_new_tokens<KV, D>(a, u.h, q0, q_len, fr.pmin, lo, hi);
+  wait_vmcnt<0>();   // the first id chunks and the query rows have landed, and the stores have completed
+  if (stored) __syncthreads();   // before any wave's page loads can read a stored token
   f16x8 qf[NT][G::KS];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {

@@ -67,64 +67,16 @@ __global__ void __launch_bounds__(256) kv_store_kernel(StoreLaunch a) {
     // CH threads (consecutive lanes of one wave, all active or all skipped)
     float ks = a.k_scale, vs = a.v_scale;
     if constexpr (KV == KV_I8T) {
-      float km = 0.0f, vm = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        km = fmaxf(km, fabsf(kf[i]));
-        vm = fmaxf(vm, fabsf(vf[i]));
-      }
-#pragma unroll
-      for (int o = 1; o < CH; o <<= 1) {
-        km = fmaxf(km, __shfl_xor(km, o));
-        vm = fmaxf(vm, __shfl_xor(vm, o));
-      }
-      ks = km / 127.0f;   // correctly rounded (built with -fhip-fp32-correctly-rounded-divide-sqrt)
-      vs = vm / 127.0f;
+      ks = row_absmax(kf, CH) / 127.0f;   // correctly rounded (built with -fhip-fp32-correctly-rounded-divide-sqrt)
+      vs = row_absmax(vf, CH) / 127.0f;
       if (c == 0) {
         const int64_t si = (page * a.hkv + h) * kPage + tp;
         a.k_scales[si] = ks;
         a.v_scales[si] = vs;
       }
     }
-    uint32_t kcode[8], vcode[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if constexpr (KV == KV_F16) {
-        kcode[i] = as<uint16_t>((f16)kf[i]);
-        vcode[i] = as<uint16_t>((f16)vf[i]);
-      } else if constexpr (KV == KV_E4M3) {
-        kcode[i] = e4m3_encode(kf[i] / a.k_scale);
-        vcode[i] = e4m3_encode(vf[i] / a.v_scale);
-      } else if constexpr (KV == KV_I8) {
-        kcode[i] = (uint32_t)i8_encode(kf[i] / ks) & 0xFFu;
-        vcode[i] = (uint32_t)i8_encode(vf[i] / vs) & 0xFFu;
-      } else {            // a zero row (scale 0) codes to 0
-        kcode[i] = ks > 0.0f ? (uint32_t)i8_encode(kf[i] / ks) & 0xFFu : 0u;
-        vcode[i] = vs > 0.0f ? (uint32_t)i8_encode(vf[i] / vs) & 0xFFu : 0u;
-      }
-    }
-
-    // K: the 8 dims are contiguous inside one 16-byte piece of the layout.
-    const uint32_t koff = k_elem_offset<D, E>(tp, d0);
-    if constexpr (E == 2) {
-      u32x4 w;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) w[j] = kcode[2 * j] | (kcode[2 * j + 1] << 16);
-      *reinterpret_cast<u32x4*>(kc + koff) = w;
-    } else {
-      u32x2 w;
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        w[j] = kcode[4 * j] | (kcode[4 * j + 1] << 8) | (kcode[4 * j + 2] << 16) | (kcode[4 * j + 3] << 24);
-      *reinterpret_cast<u32x2*>(kc + koff) = w;
-    }
-    // V: one element per store.
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t voff = v_elem_offset<D, E>(tp, d0 + i);
-      if constexpr (E == 2) *reinterpret_cast<uint16_t*>(vc + voff) = (uint16_t)vcode[i];
-      else vc[voff] = (uint8_t)vcode[i];
-    }
+    store_row8<KV, D>(kc, tp, d0, kf, ks, false);
+    store_row8<KV, D>(vc, tp, d0, vf, vs, true);
   }
 }
 

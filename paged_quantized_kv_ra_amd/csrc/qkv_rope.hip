@@ -55,14 +55,6 @@ __device__ __forceinline__ u32x4 pack8(const float (&y)[8]) {
   return w;
 }
 
-template <int KV>
-__device__ __forceinline__ uint32_t encode(float x, float scale) {
-  if constexpr (KV == KV_F16) return as<uint16_t>((f16)x);
-  else if constexpr (KV == KV_E4M3) return e4m3_encode(x / scale);
-  else if constexpr (KV == KV_I8) return (uint32_t)i8_encode(x / scale) & 0xFFu;
-  else return scale > 0.0f ? (uint32_t)i8_encode(x / scale) & 0xFFu : 0u;   // a zero row codes to 0
-}
-
 template <int KV, int D, bool BF16>
 __global__ void __launch_bounds__(256) qkv_rope_kernel(RopeLaunch a) {
   constexpr int E = KV == KV_F16 ? 2 : 1;
@@ -134,46 +126,8 @@ __global__ void __launch_bounds__(256) qkv_rope_kernel(RopeLaunch a) {
     }
     uint8_t* blk = reinterpret_cast<uint8_t*>(is_v ? a.v_cache : a.k_cache) +
                    (page * a.hkv + h) * (int64_t)(kPage * D * E);
-    uint32_t ca[8], cb[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      ca[i] = encode<KV>(xa[i], sc);
-      cb[i] = encode<KV>(xb[i], sc);
-    }
-    if (!is_v) {
-      // K: 8 consecutive dims are contiguous inside one 16-byte piece of the layout
-#pragma unroll
-      for (int part = 0; part < 2; ++part) {
-        const uint32_t* cc = part ? cb : ca;
-        uint8_t* p = blk + k_elem_offset<D, E>(tp, part ? db : da);
-        if constexpr (E == 2) {
-          u32x4 w;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) w[j] = cc[2 * j] | (cc[2 * j + 1] << 16);
-          *reinterpret_cast<u32x4*>(p) = w;
-        } else {
-          u32x2 w;
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            w[j] = cc[4 * j] | (cc[4 * j + 1] << 8) | (cc[4 * j + 2] << 16) | (cc[4 * j + 3] << 24);
-          *reinterpret_cast<u32x2*>(p) = w;
-        }
-      }
-    } else {
-      // V interleaves four tokens per dim: one element per store
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t oa = v_elem_offset<D, E>(tp, da + i);
-        const uint32_t ob = v_elem_offset<D, E>(tp, db + i);
-        if constexpr (E == 2) {
-          *reinterpret_cast<uint16_t*>(blk + oa) = (uint16_t)ca[i];
-          *reinterpret_cast<uint16_t*>(blk + ob) = (uint16_t)cb[i];
-        } else {
-          blk[oa] = (uint8_t)ca[i];
-          blk[ob] = (uint8_t)cb[i];
-        }
-      }
-    }
+    store_row8<KV, D>(blk, tp, da, xa, sc, is_v);
+    store_row8<KV, D>(blk, tp, db, xb, sc, is_v);
   }
 }
 

@@ -163,11 +163,35 @@ int32_t check_attn_pointers(const ra_attn_args* a, const Plan& p) {
     if (!aligned16(a->partial_out))
       return fail(RA_ERR_MISALIGNED, "ra_paged_attn: partial_out must be 16-byte aligned");
   }
+  if (a->new_k) {   // fused store of the query tokens' K/V
+    const int64_t g = a->num_q_heads / a->num_kv_heads;
+    if (g * a->max_q_len > ra::kMfmaRowsPerBlock)
+      return fail(RA_ERR_UNSUPPORTED,
+                  "ra_paged_attn: the fused store needs (Hq / Hkv) * max_q_len <= %d (got %lld); store longer "
+                  "blocks with ra_kv_store first", ra::kMfmaRowsPerBlock, (long long)(g * a->max_q_len));
+    if (!a->new_v || !a->new_slots)
+      return fail(RA_ERR_INVALID_ARG, "ra_paged_attn: the fused store needs new_v and new_slots with new_k");
+    if (a->new_dtype != RA_F16 && a->new_dtype != RA_BF16)
+      return fail(RA_ERR_UNSUPPORTED, "ra_paged_attn: new_dtype %d is not RA_F16 or RA_BF16", a->new_dtype);
+    const int64_t row = (int64_t)a->num_kv_heads * a->head_dim;
+    if (a->new_k_stride < row || a->new_v_stride < row)
+      return fail(RA_ERR_INVALID_ARG, "ra_paged_attn: new_k_stride / new_v_stride (%lld, %lld) smaller than "
+                  "num_kv_heads * head_dim", (long long)a->new_k_stride, (long long)a->new_v_stride);
+    if (!aligned16(a->new_k) || !aligned16(a->new_v) || (a->new_k_stride % 8) || (a->new_v_stride % 8))
+      return fail(RA_ERR_MISALIGNED, "ra_paged_attn: new_k and new_v must be 16-byte aligned and their strides "
+                  "multiples of 8");
+  }
   return RA_OK;
 }
 
 ra::AttnLaunch make_launch(const ra_attn_args* a, const Plan& p) {
   ra::AttnLaunch L{};
+  L.new_k = a->new_k;
+  L.new_v = a->new_v;
+  L.new_bf16 = a->new_dtype == RA_BF16;
+  L.new_k_stride = a->new_k_stride;
+  L.new_v_stride = a->new_v_stride;
+  L.new_slots = a->new_slots;
   L.q = a->q;
   L.q_bf16 = a->q_dtype == RA_BF16;
   L.out = p.direct ? a->out : nullptr;

@@ -128,6 +128,64 @@ __device__ __forceinline__ uint32_t v_elem_offset(int t, int d) {
 }
 
 // ---------------------------------------------------------------------------
+// The store's quantiser for one cache element: FP16 cache: RNE cast; E4M3 /
+// INT8: correctly rounded fp32 division by the scale, then the encoder (a
+// per-token INT8 row of scale 0, all zeros, codes to 0).
+template <int KV>
+__device__ __forceinline__ uint32_t encode_code(float x, float scale) {
+  if constexpr (KV == KV_F16) return as<uint16_t>((f16)x);
+  else if constexpr (KV == KV_E4M3) return e4m3_encode(x / scale);
+  else if constexpr (KV == KV_I8) return (uint32_t)i8_encode(x / scale) & 0xFFu;
+  else return scale > 0.0f ? (uint32_t)i8_encode(x / scale) & 0xFFu : 0u;
+}
+
+// Quantise dims d0 .. d0 + 7 of one token's row and write them into the
+// (page, head) block `blk` at token-in-page tp.  K: the 8 dims are contiguous
+// inside one 16-byte piece of the layout (one 8- or 16-byte store).  V:
+// four tokens interleave per dim, so one store per element.
+template <int KV, int D>
+__device__ __forceinline__ void store_row8(uint8_t* blk, int tp, int d0, const float (&x)[8], float scale,
+                                           bool is_v) {
+  constexpr int E = KV == KV_F16 ? 2 : 1;
+  uint32_t code[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) code[i] = encode_code<KV>(x[i], scale);
+  if (!is_v) {
+    uint8_t* p = blk + k_elem_offset<D, E>(tp, d0);
+    if constexpr (E == 2) {
+      u32x4 w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = code[2 * j] | (code[2 * j + 1] << 16);
+      *reinterpret_cast<u32x4*>(p) = w;
+    } else {
+      u32x2 w;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        w[j] = code[4 * j] | (code[4 * j + 1] << 8) | (code[4 * j + 2] << 16) | (code[4 * j + 3] << 24);
+      *reinterpret_cast<u32x2*>(p) = w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t off = v_elem_offset<D, E>(tp, d0 + i);
+      if constexpr (E == 2) *reinterpret_cast<uint16_t*>(blk + off) = (uint16_t)code[i];
+      else blk[off] = (uint8_t)code[i];
+    }
+  }
+}
+
+
+// fp32 max |x| of a per-token INT8 row spread over `lanes` consecutive lanes
+// (a power of two; all of them active) holding 8 values each.
+__device__ __forceinline__ float row_absmax(const float (&x)[8], int lanes) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[i]));
+  for (int o = 1; o < lanes; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+  return m;
+}
+
+// ---------------------------------------------------------------------------
 // 16-byte global load (one lane's piece of a 1 KiB wavefront slab).
 
 __device__ __forceinline__ u32x4 load16(const void* p) {

@@ -112,6 +112,13 @@ struct AttnLaunch {
   const float* v_scales;
   const int32_t* kv_pos0;  // [batch] global position of cache key 0, or nullptr (0)
   const int32_t* q_pos0;   // [batch] global position of the block's first query, or nullptr
+  // fused store of the query tokens' own K/V rows (nullptr: none)
+  const void* new_k;       // [total_q][hkv][head_dim] fp16 / bf16, new_k_stride elements per token
+  const void* new_v;
+  bool new_bf16;
+  int64_t new_k_stride;
+  int64_t new_v_stride;
+  const int64_t* new_slots;  // [total_q] cache slot of each query token
 };
 
 // Rows of a (sequence, KV head) unit: g * q_len, in 16-row matrix-core tiles

@@ -47,7 +47,7 @@ def test_exports_every_declared_symbol():
 
 def test_abi_version():
     L = _lib()
-    assert L.abi_version() == 3001
+    assert L.abi_version() == 4001
 
 
 @pytest.mark.parametrize("cname,pyname", [("ra_attn_args", "AttnArgs"), ("ra_qkv_rope_args", "RopeArgs")])
@@ -424,3 +424,27 @@ def test_rope_table_validation():
     assert lib.ra_rope_table(buf, 4, 16, 10000.0, 2.0, 0, 32.0, 1.0) == 1
     assert lib.ra_rope_table(None, 4, 16, 10000.0, 1.0, 0, 32.0, 1.0) == 1
     assert lib.ra_rope_table(buf, 4, 16, 10000.0, 2.0, 64, 32.0, 1.0) == 0
+
+
+BAD_FUSED = [
+    (dict(max_q_len=7, min_q_len=1), 2, "fused store"),       # 8 * 7 = 56 rows > 48
+    (dict(new_v=None), 1, "new_v and new_slots"),
+    (dict(new_slots=None), 1, "new_v and new_slots"),
+    (dict(new_dtype=3), 2, "new_dtype"),
+    (dict(new_k_stride=128), 1, "new_k_stride"),
+    (dict(new_v_stride=2 * 128 + 4), 3, "16-byte aligned"),
+    (dict(new_k=FAKE + 8), 3, "16-byte aligned"),
+]
+
+
+@pytest.mark.parametrize("kw,status,msg", BAD_FUSED, ids=[f"{i}-{m}" for i, (_, _, m) in enumerate(BAD_FUSED)])
+def test_fused_store_validation(kw, status, msg):
+    L = _lib()
+    lib = L.load_library()
+    base = dict(new_k=FAKE, new_v=FAKE, new_dtype=L.RA_F16, new_k_stride=2 * 128, new_v_stride=2 * 128,
+                new_slots=FAKE)
+    base.update(kw)
+    a = _good_args(L, **base)
+    st = lib.ra_paged_attn(ctypes.byref(a), None)
+    assert st == status, (st, lib.ra_last_error())
+    assert msg in lib.ra_last_error().decode()
