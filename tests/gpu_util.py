@@ -30,9 +30,12 @@ def t_src(x, dtype, device="cuda"):
 
 
 class DeviceWorkload:
-    """A workload's caches filled through ra_kv_store, plus device metadata."""
+    """A workload's caches filled through ra_kv_store, plus device metadata.
 
-    def __init__(self, w, device="cuda", chunk_tokens=1 << 18, store=True):
+    fused_new=True leaves the step's query tokens out of the stores: attn()
+    then stores them itself (the attention launch's fused store)."""
+
+    def __init__(self, w, device="cuda", chunk_tokens=1 << 18, store=True, fused_new=False):
         import paged_quantized_kv_ra_amd as P
         self.w = w
         D, hkv = w.head_dim, w.num_kv_heads
@@ -42,13 +45,21 @@ class DeviceWorkload:
         if w.kv_dtype == "int8_tok":          # unwritten scales read as NaN
             self.k_scales = P.new_scale_plane(w.num_pages, hkv, device)
             self.v_scales = P.new_scale_plane(w.num_pages, hkv, device)
+        self.fused = None
+        rows = np.arange(w.tokens_k.shape[0])
+        if fused_new:
+            new_rows = w.new_token_rows()
+            rows = np.setdiff1d(rows, new_rows)
+            self.fused = dict(new_k=t_src(w.tokens_k[new_rows], w.src_dtype, device),
+                              new_v=t_src(w.tokens_v[new_rows], w.src_dtype, device),
+                              new_slots=torch.from_numpy(w.token_slots[new_rows]).to(device))
         if store:
-            U = w.tokens_k.shape[0]
+            U = rows.size
             for lo in range(0, U, chunk_tokens):
-                hi = min(U, lo + chunk_tokens)
-                k = t_src(w.tokens_k[lo:hi], w.src_dtype, device)
-                v = t_src(w.tokens_v[lo:hi], w.src_dtype, device)
-                s = torch.from_numpy(w.token_slots[lo:hi]).to(device)
+                r = rows[lo:min(U, lo + chunk_tokens)]
+                k = t_src(w.tokens_k[r], w.src_dtype, device)
+                v = t_src(w.tokens_v[r], w.src_dtype, device)
+                s = torch.from_numpy(w.token_slots[r]).to(device)
                 P.kv_store(k, v, s, self.k_cache, self.v_cache, w.kv_dtype, w.k_scale, w.v_scale,
                            k_scales=self.k_scales, v_scales=self.v_scales)
         self.q = t_src(w.q, w.q_dtype, device)
@@ -65,7 +76,8 @@ class DeviceWorkload:
                             min_q_len=int(w.q_len.min()), max_context_len=w.max_context_len,
                             window_left=w.window_left, num_sinks=w.num_sinks,
                             num_splits=w.num_splits if num_splits is None else num_splits,
-                            partials_only=partials_only, k_scales=self.k_scales, v_scales=self.v_scales, **kw)
+                            partials_only=partials_only, k_scales=self.k_scales, v_scales=self.v_scales,
+                            **(self.fused or {}), **kw)
 
 
 def dequant_tokens(w, rows, which, heads=None):

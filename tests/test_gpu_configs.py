@@ -5,7 +5,9 @@ Store: bit-exact on a random sample of tokens (their bytes in the GPU caches
 against the oracle's codes at the layout's offsets) plus the untouched
 sentinel of an unused page.  Attention: every output of sampled
 (sequence, KV head) units against the fp64 oracle computed one unit at a
-time.
+time.  As in bench.py, decode and verify workloads (at most 48 rows per KV
+head) store the step's own tokens inside the attention launch; the store
+sample is drawn after it and always includes some of those tokens.
 """
 import numpy as np
 import pytest
@@ -47,9 +49,11 @@ def _query_sample(w, b, seed):
     return np.unique(np.clip(rows, 0, ql - 1))
 
 
-def _check_store_sample(w, dw, n=48, seed=0):
+def _check_store_sample(w, dw, n=48, seed=0, extra_rows=None):
     rng = np.random.default_rng(seed)
     rows = rng.choice(w.tokens_k.shape[0], size=min(n, w.tokens_k.shape[0]), replace=False)
+    if extra_rows is not None:
+        rows = np.unique(np.concatenate([rows, extra_rows]))
     slots = w.token_slots[rows]
     pages = np.unique(slots // 16)
     e = 2 if w.kv_dtype == "f16" else 1
@@ -80,13 +84,14 @@ def _check_store_sample(w, dw, n=48, seed=0):
 def _run(name, make, units, base=None):
     with Timer(f"{name}: build"):
         w = make() if base is None else make(base)
+    fused = (w.num_q_heads // w.num_kv_heads) * w.max_q_len <= 48
     with Timer(f"{name}: upload + store"):
-        dw = DeviceWorkload(w)
+        dw = DeviceWorkload(w, fused_new=fused)
         torch.cuda.synchronize()
-    _check_store_sample(w, dw)
-    with Timer(f"{name}: attention"):
+    with Timer(f"{name}: attention{' with the fused store' if fused else ''}"):
         out, lse = dw.attn()
         torch.cuda.synchronize()
+    _check_store_sample(w, dw, extra_rows=w.new_token_rows()[:8] if fused else None)
     out = out_to_np(out)
     lse = lse.cpu().numpy().astype(np.float64)
     for unit in units:
