@@ -330,11 +330,13 @@ __device__ __forceinline__ bool store_new_tokens(const AttnLaunch& a, int h, int
                             row * (is_v ? a.new_v_stride : a.new_k_stride) + (int64_t)h * D + 8 * c;
       const u32x4 raw = load16(src);
       const int64_t slot = a.new_slots[row];
+      asm volatile("" ::"v"(raw), "v"(slot));   // both requests in flight before the first wait
       float x[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const uint16_t b = (uint16_t)(raw[j >> 1] >> (16 * (j & 1)));
-        x[j] = a.new_bf16 ? bf16_to_f32(b) : (float)as<f16>(b);
+        const float hv = (float)as<f16>(b), bv = bf16_to_f32(b);
+        x[j] = a.new_bf16 ? bv : hv;
       }
       float sc = is_v ? a.v_scale : a.k_scale;
       if constexpr (KV == KV_I8T) sc = row_absmax(x, CH) / 127.0f;   // correctly rounded division
