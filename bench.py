@@ -37,7 +37,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_HBM_GBS = 8000.0
 PEAK_F16_TFLOPS = 2500.0      # dense fp16 matrix-core peak (the path's MFMA dtype)
 POOL_ROTATION_BYTES = 1 << 30
-KERNEL_SOURCES = ["paged_quantized_kv_ra_amd/csrc/attn_mfma.hip",
+KERNEL_SOURCES = ["paged_quantized_kv_ra_amd/csrc/attn_mfma.hip", "paged_quantized_kv_ra_amd/csrc/attn_prefill.hip",
                   "paged_quantized_kv_ra_amd/csrc/attn_common.h", "paged_quantized_kv_ra_amd/csrc/ra_device.h",
                   "paged_quantized_kv_ra_amd/csrc/ra_internal.h"]
 
@@ -434,7 +434,9 @@ def main():
         f"attention {attn_avg_ms * 1e3:.1f} us avg, {achieved:.0f} GB/s algorithmic, {tflops:.1f} TFLOP/s")
     if prefill:
         roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(tflops / PEAK_F16_TFLOPS, 4), "traffic": traffic, "kernel": "attn_mfma_kernel",
+                "frac": round(tflops / PEAK_F16_TFLOPS, 4), "traffic": traffic,
+                "kernel": "attn_prefill_kernel" if w.kv_dtype in ("e4m3", "int8") and w.head_dim == 128
+                and w.window_left < 0 and w.max_context_len <= 2 * int(w.q_len.min()) else "attn_mfma_kernel",
                 "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": alg,
                 "attn_us": round(attn_avg_ms * 1e3, 2), "kernel_source_hash": src_hash}
     else:

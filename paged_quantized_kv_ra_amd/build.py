@@ -56,6 +56,7 @@ def torch_lib_dir():
 # waves per SIMD and avoids AGPR <-> VGPR copies around the softmax.
 FILE_FLAGS = {
     "attn_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "attn_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

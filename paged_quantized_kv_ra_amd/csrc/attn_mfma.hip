@@ -450,6 +450,7 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
   const int32_t row0 = u.rg * kMfmaRowsPerBlock;
   if (row0 >= rows) return;
   const int32_t ctx = a.context_lens[u.b];
+  if (prefill_sequence(a, rows, ctx, q_len)) return;   // the prefill kernel's sequence
   const int32_t kv0 = a.kv_pos0 ? a.kv_pos0[u.b] : 0;
   const int32_t qp0 = a.q_pos0 ? a.q_pos0[u.b] : 0;
   bool bad = !seq_ok(a, ctx, q0, q1, kv0, qp0);

@@ -321,8 +321,25 @@ int32_t ra_paged_attn(const ra_attn_args* args, void* stream) {
   hipError_t e = hipSuccess;
   L.part_tokens = p.part_large;
   L.part_small = p.part_small;
-  e = ra::launch_attn_mfma(L, s);
-  if (e != hipSuccess) return fail(RA_ERR_HIP, "ra_paged_attn: attention kernel launch failed: %s", hipGetErrorString(e));
+  // long query blocks (more than kPrefillMinRows rows per KV head) go to the
+  // prefill kernel when the call's constants allow; the decode kernel's grid
+  // then covers only the shorter blocks
+  const int32_t g = args->num_q_heads / args->num_kv_heads;
+  L.prefill = ra::prefill_kernel_serves(L) && (int64_t)g * args->max_q_len > ra::kPrefillMinRows;
+  // the decode kernel is skipped only when the host bounds prove every
+  // sequence is the prefill kernel's (a batch of cold prompts)
+  const bool all_prefill = L.prefill && (int64_t)g * args->min_q_len > ra::kPrefillMinRows &&
+                           (int64_t)args->max_context_len <= 2 * (int64_t)args->min_q_len;
+  if (!all_prefill) {
+    e = ra::launch_attn_mfma(L, s);
+    if (e != hipSuccess)
+      return fail(RA_ERR_HIP, "ra_paged_attn: attention kernel launch failed: %s", hipGetErrorString(e));
+  }
+  if (L.prefill) {
+    e = ra::launch_attn_prefill(L, s);
+    if (e != hipSuccess)
+      return fail(RA_ERR_HIP, "ra_paged_attn: prefill kernel launch failed: %s", hipGetErrorString(e));
+  }
   if (!p.direct && args->out) {
     ra::MergeLaunch M{args->partial_out, args->partial_lse, p.slots, (int64_t)args->total_q * args->num_q_heads,
                       args->head_dim, args->out, args->q_dtype, args->lse};

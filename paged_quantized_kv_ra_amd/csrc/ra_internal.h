@@ -119,6 +119,7 @@ struct AttnLaunch {
   int64_t new_k_stride;
   int64_t new_v_stride;
   const int64_t* new_slots;  // [total_q] cache slot of each query token
+  bool prefill;            // the prefill kernel takes the sequences prefill_sequence() selects
 };
 
 // Rows of a (sequence, KV head) unit: g * q_len, in 16-row matrix-core tiles
@@ -142,6 +143,21 @@ constexpr int kSmallSplits = 32;
 constexpr int kFillUnits = 2048;
 
 hipError_t launch_attn_mfma(const AttnLaunch& a, hipStream_t s);
+
+// Long query blocks (prefill): a sequence with more than kPrefillMinRows rows
+// per KV head is attended by the prefill kernel (rows split over waves, each
+// 64-key tile decoded once per workgroup) when the call's constants allow it
+// (FP8 E4M3 or INT8 with per-layer scales, head_dim 128, no window) ...
+constexpr int kPrefillMinRows = 256;
+// ... and whose block is at least half of its context (cold prompts and early
+// chunks, whose causal row groups see few keys each; a short chunk after a
+// long cached context streams better through the decode kernel, whose waves
+// split the keys)
+__host__ __device__ inline bool prefill_sequence(const AttnLaunch& a, int32_t rows, int32_t ctx, int32_t q_len) {
+  return a.prefill && rows > kPrefillMinRows && (int64_t)ctx <= 2 * (int64_t)q_len;
+}
+bool prefill_kernel_serves(const AttnLaunch& a);
+hipError_t launch_attn_prefill(const AttnLaunch& a, hipStream_t s);
 
 struct MergeLaunch {
   const float* part_out;

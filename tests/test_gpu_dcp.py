@@ -28,6 +28,8 @@ CASES = [
     ("g3_int8_q1_split2", [2500, 999, 130], 1, 16, 2, 128, "int8", -1, 0, [0.2, 0.71], 2),
     ("g3_e4m3_q16_window_sinks", [3000, 1700], 16, 16, 2, 128, "e4m3", 300, 4, [0.001, 0.9], 0),
     ("g2_int8tok_q5_d64", [1500, 600, 17], 5, 8, 2, 64, "int8_tok", -1, 0, [0.5], 3),
+    # a 300-token prefill chunk per sequence (the prefill kernel's rows)
+    ("g2_e4m3_prefill_q300", [1500, 700], 300, 16, 2, 128, "e4m3", -1, 0, [0.4], 0),
 ]
 
 
