@@ -20,8 +20,10 @@ Prefill workloads (whole prompts or prompt chunks as the query block) report
 query tokens per second instead, and an MFMA roofline in TFLOP/s (4 * D
 flops per visible (query head, key) pair); with one partition slot the
 attention writes its output directly and there is no merge.
-``--fused-qkv`` stores the new tokens from packed QKV rows with RoPE
-(ra_qkv_rope_store, which also writes the rotated Q) instead of ra_kv_store.
+``--fused-qkv`` takes the new tokens from packed QKV rows with RoPE: for
+decode and verify blocks the attention launch rotates Q and K and stores K/V
+itself; prefill blocks use ra_qkv_rope_store (which also writes the rotated
+Q) first.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--fused-qkv] [--gpus 1]
 """
@@ -134,19 +136,39 @@ class Step:
         self.out = torch.empty_like(self.q)
         self.lse = torch.empty((T, hq), dtype=torch.float32, device=dev)
         # decode and verify blocks (at most 48 rows per KV head) store their new
-        # tokens inside the attention launch; prefill blocks, --separate-store
-        # and --fused-qkv store them with a launch of their own first
+        # tokens inside the attention launch (with --fused-qkv also rotating Q
+        # and K by RoPE there); prefill blocks and --separate-store store them
+        # with a launch of their own first
         g = w.num_q_heads // hkv
-        self.store_mode = ("qkv_rope_store" if fused_qkv else
-                           "kv_store" if separate_store or g * w.max_q_len > 48 else "fused")
-        fused = self.store_mode == "fused"
+        in_launch = not separate_store and g * w.max_q_len <= 48
+        if fused_qkv:
+            self.store_mode = "fused_rope" if in_launch else "qkv_rope_store"
+        else:
+            self.store_mode = "fused" if in_launch else "kv_store"
+        if fused_qkv:
+            # packed QKV rows of the new tokens (fp16), their positions, and
+            # the library's YaRN table (factor 2 over half the positions used)
+            from paged_quantized_kv_ra_amd import workloads as W
+            assert w.q_dtype == "f16" and self.k_new.shape[0] == T
+            pos, _ = W.step_positions_and_slots(w)
+            self.qkv = self._src(W.packed_qkv(w.seed, T, hq, hkv, D, "f16"))
+            self.positions = torch.from_numpy(pos).to(dev)
+            max_pos = int(pos.max()) + 1
+            self.table = P.rope_table(max_pos, D, 1e6, 2.0, max(1, max_pos // 2), device=dev)
+        q_in, k_in, v_in, rope = self.q, self.k_new, self.v_new, {}
+        if self.store_mode == "fused_rope":   # Q, K and V straight from the packed rows
+            q_in = self.qkv[:, :hq * D].view(T, hq, D)
+            k_in = self.qkv[:, hq * D:(hq + hkv) * D].view(T, hkv, D)
+            v_in = self.qkv[:, (hq + hkv) * D:].view(T, hkv, D)
+            rope = dict(rope_table=self.table, positions=self.positions, rotary_dim=D)
+        fused = self.store_mode in ("fused", "fused_rope")
         self.args = []
         for k, v, ks, vs in self.pools:
-            a = L._attn_args(self.q, k, v, self.bt, self.ctx, self.qsl, w.kv_dtype, w.k_scale, w.v_scale,
+            a = L._attn_args(q_in, k, v, self.bt, self.ctx, self.qsl, w.kv_dtype, w.k_scale, w.v_scale,
                              w.softmax_scale, w.max_q_len, int(w.q_len.min()), w.max_context_len,
                              w.window_left, w.num_sinks, w.num_splits, hkv, ks, vs,
-                             new_k=self.k_new if fused else None, new_v=self.v_new if fused else None,
-                             new_slots=self.slots_new if fused else None)
+                             new_k=k_in if fused else None, new_v=v_in if fused else None,
+                             new_slots=self.slots_new if fused else None, **rope)
             self.args.append(a)
         self.slots, po_n, _ = L.paged_attn_workspace(self.args[0])
         # one partition slot (a long prefill chunk): the kernel writes out and
@@ -167,16 +189,7 @@ class Step:
         self.q_code = L.RA_F16 if w.q_dtype == "f16" else L.RA_BF16
         self.kv_code = L.KV_CODES[w.kv_dtype]
         self.rope_args = None
-        if fused_qkv:
-            # packed QKV rows of the new tokens (fp16), their positions, and
-            # the library's YaRN table (factor 2 over half the positions used)
-            from paged_quantized_kv_ra_amd import workloads as W
-            assert w.q_dtype == "f16" and self.k_new.shape[0] == T
-            pos, slots = W.step_positions_and_slots(w)
-            self.qkv = self._src(W.packed_qkv(w.seed, T, hq, hkv, D, "f16"))
-            self.positions = torch.from_numpy(pos).to(dev)
-            max_pos = int(pos.max()) + 1
-            self.table = P.rope_table(max_pos, D, 1e6, 2.0, max(1, max_pos // 2), device=dev)
+        if self.store_mode == "qkv_rope_store":
             self.rope_args = [L._rope_args(self.qkv, self.positions, self.table, D, hq, hkv, D, self.q,
                                            self.slots_new, k, v, w.kv_dtype, w.k_scale, w.v_scale, ks, vs)
                               for k, v, ks, vs in self.pools]
@@ -204,7 +217,7 @@ class Step:
         w, lib, L = self.w, self.lib, self.L
         k, v, ks, vs = self.pools[i % self.copies]
         s = ctypes.c_void_p(stream)
-        if self.store_mode == "fused":
+        if self.store_mode in ("fused", "fused_rope"):
             st = 0                   # the attention launch stores the new tokens itself
         elif self.rope_args is not None:
             st = lib.ra_qkv_rope_store(ctypes.byref(self.rope_args[i % self.copies]), s)

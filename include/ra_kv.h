@@ -88,7 +88,7 @@
 extern "C" {
 #endif
 
-#define RA_KV_ABI_VERSION 4
+#define RA_KV_ABI_VERSION 5
 #define RA_KV_LAYOUT_ID 1
 #define RA_KV_PAGE_SIZE 16
 #define RA_KV_MAX_SPLITS 4096
@@ -277,6 +277,15 @@ int32_t ra_qkv_rope_store(const ra_qkv_rope_args* args, void* stream);
  * 48; longer blocks (prefill) return RA_ERR_UNSUPPORTED and are stored with
  * ra_kv_store first.  The store's format, scales and rounding are those of
  * ra_kv_store (per-token INT8 writes its scale planes too).
+ *
+ * RoPE on the fused path: with rope_table non-NULL (and new_k), query token
+ * q's Q rows and its K rows are rotated by the table row positions[q] exactly
+ * as ra_qkv_rope_store rotates them (same pairing, fp32 without fused
+ * multiply-add, rotated Q rounded to q_dtype) before use: one launch then
+ * does the whole of ra_qkv_rope_store + ra_paged_attn for a decode or verify
+ * step.  q (q_token_stride elements between tokens) and new_k / new_v may
+ * point into the packed QKV projection rows.  A position outside
+ * [0, rope_max_position) gives NaN rows for that token and stores nothing.
  * With more than
  * one partition slot the kernel writes partial_out [slots][total_q][Hq][D] and
  * partial_lse [slots][total_q][Hq] (fp32; out already normalised; an empty
@@ -328,6 +337,13 @@ typedef struct ra_attn_args {
   int64_t new_k_stride;            /* elements between tokens, multiple of 8     */
   int64_t new_v_stride;
   const int64_t* new_slots;        /* [total_q] cache slot of each query token   */
+  int64_t q_token_stride;          /* elements between query tokens; 0: Hq * D   */
+  /* RoPE on the fused path: q and new_k hold rows before the rotation; NULL
+     rope_table rotates nothing.  Needs new_k (decode and verify blocks). */
+  const float* rope_table;         /* [rope_max_position][2][rotary_dim / 2]     */
+  int32_t rope_max_position;
+  int32_t rotary_dim;              /* multiple of 16, <= head_dim                */
+  const int64_t* positions;        /* [total_q] RoPE position of each query token*/
 } ra_attn_args;
 
 /*

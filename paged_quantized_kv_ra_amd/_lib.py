@@ -72,6 +72,11 @@ class AttnArgs(_c.Structure):
         ("new_k_stride", _c.c_int64),
         ("new_v_stride", _c.c_int64),
         ("new_slots", _vp),
+        ("q_token_stride", _c.c_int64),
+        ("rope_table", _vp),
+        ("rope_max_position", _c.c_int32),
+        ("rotary_dim", _c.c_int32),
+        ("positions", _vp),
     ]
 
 
@@ -219,8 +224,9 @@ def kv_store(k, v, slot_mapping, k_cache, v_cache, kv_dtype, k_scale=1.0, v_scal
 def _attn_args(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, kv_dtype, k_scale,
                v_scale, softmax_scale, max_q_len, min_q_len, max_context_len, window_left, num_sinks,
                num_splits, num_kv_heads, k_scales=None, v_scales=None, kv_pos0=None, q_pos0=None, new_k=None,
-               new_v=None, new_slots=None):
+               new_v=None, new_slots=None, rope_table=None, positions=None, rotary_dim=None):
     T, hq, D = q.shape
+    assert q.stride(2) == 1 and q.stride(1) == D, "query heads must be contiguous rows of head_dim"
     a = AttnArgs()
     a.struct_size = _c.sizeof(AttnArgs)
     a.q_dtype = _src_code(q)
@@ -261,6 +267,13 @@ def _attn_args(q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
         a.new_k_stride = new_k.stride(0)
         a.new_v_stride = new_v.stride(0)
         a.new_slots = new_slots.data_ptr()
+    a.q_token_stride = q.stride(0) if q.stride(0) != hq * D else 0
+    if rope_table is not None:       # RoPE on the fused path
+        assert rope_table.dtype == torch.float32 and rope_table.is_contiguous() and positions.dtype == torch.int64
+        a.rope_table = rope_table.data_ptr()
+        a.rope_max_position = rope_table.shape[0]
+        a.rotary_dim = int(rotary_dim if rotary_dim is not None else rope_table.shape[2] * 2)
+        a.positions = positions.data_ptr()
     return a
 
 
@@ -276,7 +289,7 @@ def paged_attn(q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
                max_q_len, max_context_len, k_scale=1.0, v_scale=1.0, softmax_scale=None, min_q_len=0,
                window_left=-1, num_sinks=0, num_splits=0, out=None, lse=None, partials_only=False,
                workspace=None, stream=None, k_scales=None, v_scales=None, kv_pos0=None, q_pos0=None,
-               new_k=None, new_v=None, new_slots=None):
+               new_k=None, new_v=None, new_slots=None, rope_table=None, positions=None, rotary_dim=None):
     """Attention of the query blocks over the paged caches.
 
     q [total_q][Hq][D] fp16/bf16; block_tables int32 [B][stride];
@@ -285,15 +298,19 @@ def paged_attn(q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
     partials_only=True (partial_out [S][total_q][Hq][D], partial_lse [S][total_q][Hq]).
     new_k, new_v [total_q][Hkv][D] and new_slots int64 [total_q]: the query
     tokens' own K/V, stored by the launch itself (decode and verify blocks).
+    rope_table [P][2][R/2] fp32 and positions int64 [total_q] (with new_k):
+    q and new_k are rotated by RoPE inside the launch.  q may be a view into
+    packed QKV rows (its token stride is passed on).
     """
     T, hq, D = q.shape
     hkv = k_cache.shape[1]
     a = _attn_args(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, kv_dtype, k_scale,
                    v_scale, softmax_scale, max_q_len, min_q_len, max_context_len, window_left, num_sinks,
-                   num_splits, hkv, k_scales, v_scales, kv_pos0, q_pos0, new_k, new_v, new_slots)
+                   num_splits, hkv, k_scales, v_scales, kv_pos0, q_pos0, new_k, new_v, new_slots, rope_table,
+                   positions, rotary_dim)
     if not partials_only:
         if out is None:
-            out = torch.empty_like(q)
+            out = torch.empty((T, hq, D), dtype=q.dtype, device=q.device)
         if lse is None:
             lse = torch.empty((T, hq), dtype=torch.float32, device=q.device)
         a.out = out.data_ptr()

@@ -332,15 +332,22 @@ __device__ __forceinline__ bool store_new_tokens(const AttnLaunch& a, int h, int
       const int64_t slot = a.new_slots[row];
       asm volatile("" ::"v"(raw), "v"(slot));   // both requests in flight before the first wait
       float x[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint16_t b = (uint16_t)(raw[j >> 1] >> (16 * (j & 1)));
-        const float hv = (float)as<f16>(b), bv = bf16_to_f32(b);
-        x[j] = a.new_bf16 ? bv : hv;
+      src8_to_f32(raw, a.new_bf16, x);
+      bool pos_ok = true;
+      if (a.rope != nullptr) {   // RoPE on the fused path: rotate K (V passes through)
+        const int64_t rp = a.positions[row];
+        pos_ok = rp >= 0 && rp < a.rope_max_pos;
+        const int d0 = 8 * c;
+        if (!is_v && pos_ok && d0 < a.rot) {
+          const int half = a.rot / 2;
+          float partner[8];
+          src8_to_f32(load16(src + (d0 < half ? half : -half)), a.new_bf16, partner);
+          rope8(x, partner, a.rope + rp * a.rot, d0, a.rot);
+        }
       }
       float sc = is_v ? a.v_scale : a.k_scale;
       if constexpr (KV == KV_I8T) sc = row_absmax(x, CH) / 127.0f;   // correctly rounded division
-      if (slot >= 0 && slot < limit) {
+      if (pos_ok && slot >= 0 && slot < limit) {
         const int64_t page = slot >> 4;
         const int tp = (int)(slot & 15);
         if constexpr (KV == KV_I8T) {
@@ -433,6 +440,8 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
   // per-token INT8: each ring slot's 16 K and 16 V scales
   __shared__ __attribute__((aligned(16))) float sm_scl[KV == KV_I8T ? kWaves * G::NRING * 32 : 4];
   __shared__ int32_t sm_bad[kWaves];
+  // RoPE on the fused path: the workgroup's rotated query fragments, [nt][ks][lane]
+  __shared__ f16x8 sm_q[NT][G::KS][kWave];
 
   UnitId u;
   if (!decode_unit(a, row_groups, u)) return;
@@ -500,8 +509,8 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
     const int32_t r = row0 + nt * 16 + ncol;
     qlive[nt] = r < rows && !bad;
     pos[nt] = fr.pmin + (qlive[nt] ? r / g : 0);
-    const int64_t qrow = qlive[nt] ? ((int64_t)(q0 + r / g) * a.hq + u.h * g + r % g) : 0;
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + qrow * D + kgrp * (D / 4);
+    const int64_t qtok = qlive[nt] ? q0 + r / g : 0, qhead = qlive[nt] ? u.h * g + r % g : 0;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + qtok * a.q_stride + qhead * D + kgrp * (D / 4);
 #pragma unroll
     for (int ks = 0; ks < G::KS; ++ks) qraw[nt][ks] = load16(qp + 8 * ks);
   }
@@ -511,21 +520,61 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
   wait_vmcnt<0>();   // the first id chunks and the query rows have landed, and the stores have completed
   if (stored) __syncthreads();   // before any wave's page loads can read a stored token
   f16x8 qf[NT][G::KS];
+  if (a.rope == nullptr) {
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-    for (int ks = 0; ks < G::KS; ++ks) {
-      const u32x4 w = qlive[nt] ? qraw[nt][ks] : u32x4{0, 0, 0, 0};
-      if (a.q_bf16) {
+      for (int ks = 0; ks < G::KS; ++ks) {
+        const u32x4 w = qlive[nt] ? qraw[nt][ks] : u32x4{0, 0, 0, 0};
+        if (a.q_bf16) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t word = w[i >> 1];
-          qf[nt][ks][i] = (f16)bf16_to_f32((uint16_t)(word >> (16 * (i & 1))));
+          for (int i = 0; i < 8; ++i) {
+            const uint32_t word = w[i >> 1];
+            qf[nt][ks][i] = (f16)bf16_to_f32((uint16_t)(word >> (16 * (i & 1))));
+          }
+        } else {
+          qf[nt][ks] = as<f16x8>(w);
         }
-      } else {
-        qf[nt][ks] = as<f16x8>(w);
       }
     }
+  } else {
+    // RoPE on the fused path: the workgroup rotates its query tile once,
+    // (row, 8-dim chunk) per task, as the fused QKV kernel does (fp32, no
+    // fused multiply-add, rounded to the query dtype), into LDS
+    constexpr int kTasks = NT * 16 * (D / 8);
+    for (int task = threadIdx.x; task < kTasks; task += kWaves * kWave) {
+      const int rr = task / (D / 8), ch = task % (D / 8);
+      const int32_t r = row0 + rr;
+      const int d0 = 8 * ch;
+      f16x8 outv = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (r < rows && !bad) {
+        const int64_t tok = q0 + r / g;
+        const uint16_t* rowp = reinterpret_cast<const uint16_t*>(a.q) + tok * a.q_stride + (int64_t)(u.h * g + r % g) * D;
+        float x[8];
+        src8_to_f32(load16(rowp + d0), a.q_bf16, x);
+        const int64_t rp = a.positions[tok];
+        if (rp >= 0 && rp < a.rope_max_pos) {
+          if (d0 < a.rot) {
+            const int half = a.rot / 2;
+            float partner[8];
+            src8_to_f32(load16(rowp + d0 + (d0 < half ? half : -half)), a.q_bf16, partner);
+            rope8(x, partner, a.rope + rp * a.rot, d0, a.rot);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) x[i] = __builtin_nanf("");
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) outv[i] = a.q_bf16 ? (f16)bf16_to_f32(f32_to_bf16(x[i])) : (f16)x[i];
+      }
+      // operand slot: tile rr / 16, k-step ch % (D / 32), lane (ch / (D / 32)) * 16 + rr % 16
+      sm_q[rr / 16][ch % (D / 32)][(ch / (D / 32)) * 16 + rr % 16] = outv;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < G::KS; ++ks) qf[nt][ks] = sm_q[nt][ks][lane];
   }
 
   Acc<KV, D, NT> acc;

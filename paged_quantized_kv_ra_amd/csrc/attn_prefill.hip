@@ -111,8 +111,8 @@ __global__ void __launch_bounds__(kPThreads) attn_prefill_kernel(AttnLaunch a, i
     const int32_t r = row0 + wave * (kPNT * 16) + nt * 16 + ncol;
     qlive[nt] = r < rows && !bad;
     pos[nt] = fr.pmin + (qlive[nt] ? r / g : 0);
-    const int64_t qrow = qlive[nt] ? ((int64_t)(q0 + r / g) * a.hq + h * g + r % g) : 0;
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + qrow * kPD + kgrp * (kPD / 4);
+    const int64_t qtok = qlive[nt] ? q0 + r / g : 0, qhead = qlive[nt] ? h * g + r % g : 0;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + qtok * a.q_stride + qhead * kPD + kgrp * (kPD / 4);
 #pragma unroll
     for (int ks = 0; ks < kPKS; ++ks) {
       const u32x4 w = qlive[nt] ? load16(qp + 8 * ks) : u32x4{0, 0, 0, 0};

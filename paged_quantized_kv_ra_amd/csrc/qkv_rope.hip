@@ -24,16 +24,6 @@
 namespace ra {
 namespace {
 
-// the rotation, evaluated as written: two roundings per product, one per sum
-__device__ __forceinline__ float rot_first(float x1, float x2, float c, float s) {
-#pragma clang fp contract(off)
-  return x1 * c - x2 * s;
-}
-__device__ __forceinline__ float rot_second(float x1, float x2, float c, float s) {
-#pragma clang fp contract(off)
-  return x2 * c + x1 * s;
-}
-
 template <bool BF16>
 __device__ __forceinline__ void unpack8(const u32x4& r, float (&x)[8]) {
 #pragma unroll
@@ -91,8 +81,8 @@ __global__ void __launch_bounds__(256) qkv_rope_kernel(RopeLaunch a) {
       for (int i = 0; i < 8; ++i) {
         const float co = i < 4 ? c0[i & 3] : c1[i & 3];
         const float si = i < 4 ? s0[i & 3] : s1[i & 3];
-        const float y1 = rot_first(xa[i], xb[i], co, si);
-        const float y2 = rot_second(xa[i], xb[i], co, si);
+        const float y1 = rope_first(xa[i], xb[i], co, si);
+        const float y2 = rope_second(xa[i], xb[i], co, si);
         xa[i] = y1;
         xb[i] = y2;
       }

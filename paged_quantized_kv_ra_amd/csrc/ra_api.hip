@@ -147,6 +147,22 @@ int32_t check_attn_pointers(const ra_attn_args* a, const Plan& p) {
                 "ra_paged_attn: q, k_cache, v_cache, block_tables, context_lens and query_start_loc must be non-NULL");
   if (!aligned16(a->q) || !aligned16(a->k_cache) || !aligned16(a->v_cache) || (a->out && !aligned16(a->out)))
     return fail(RA_ERR_MISALIGNED, "ra_paged_attn: q, out, k_cache and v_cache must be 16-byte aligned");
+  if (a->q_token_stride != 0) {
+    if (a->q_token_stride < (int64_t)a->num_q_heads * a->head_dim)
+      return fail(RA_ERR_INVALID_ARG, "ra_paged_attn: q_token_stride %lld smaller than num_q_heads * head_dim",
+                  (long long)a->q_token_stride);
+    if (a->q_token_stride % 8) return fail(RA_ERR_MISALIGNED, "ra_paged_attn: q_token_stride must be a multiple of 8");
+  }
+  if (a->rope_table) {
+    if (!a->new_k)
+      return fail(RA_ERR_INVALID_ARG, "ra_paged_attn: rope_table needs the fused store (new_k, new_v, new_slots)");
+    if (!a->positions) return fail(RA_ERR_INVALID_ARG, "ra_paged_attn: rope_table needs positions");
+    if (a->rotary_dim < 16 || a->rotary_dim % 16 || a->rotary_dim > a->head_dim)
+      return fail(RA_ERR_INVALID_ARG, "ra_paged_attn: rotary_dim %d must be a multiple of 16 in [16, head_dim]",
+                  a->rotary_dim);
+    if (a->rope_max_position < 1) return fail(RA_ERR_INVALID_ARG, "ra_paged_attn: rope_max_position must be >= 1");
+    if (!aligned16(a->rope_table)) return fail(RA_ERR_MISALIGNED, "ra_paged_attn: rope_table must be 16-byte aligned");
+  }
   if (a->kv_dtype == RA_KV_INT8_TOKEN) {
     if (!a->k_scales || !a->v_scales)
       return fail(RA_ERR_INVALID_ARG, "ra_paged_attn: per-token INT8 KV needs the k_scales and v_scales planes");
@@ -192,6 +208,11 @@ ra::AttnLaunch make_launch(const ra_attn_args* a, const Plan& p) {
   L.new_k_stride = a->new_k_stride;
   L.new_v_stride = a->new_v_stride;
   L.new_slots = a->new_slots;
+  L.q_stride = a->q_token_stride > 0 ? a->q_token_stride : (int64_t)a->num_q_heads * a->head_dim;
+  L.rope = a->rope_table;
+  L.rope_max_pos = a->rope_max_position;
+  L.rot = a->rotary_dim;
+  L.positions = a->positions;
   L.q = a->q;
   L.q_bf16 = a->q_dtype == RA_BF16;
   L.out = p.direct ? a->out : nullptr;

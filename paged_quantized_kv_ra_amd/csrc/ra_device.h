@@ -175,6 +175,50 @@ __device__ __forceinline__ void store_row8(uint8_t* blk, int tp, int d0, const f
 }
 
 
+// ---------------------------------------------------------------------------
+// Rotary position embedding (half-split pairing, dim i with i + R/2): the
+// pair turns as y1 = x1 c - x2 s, y2 = x2 c + x1 s, evaluated as written in
+// fp32 (two roundings per product, one per sum: no fused multiply-add).
+__device__ __forceinline__ float rope_first(float x1, float x2, float c, float s) {
+#pragma clang fp contract(off)
+  return x1 * c - x2 * s;
+}
+__device__ __forceinline__ float rope_second(float x1, float x2, float c, float s) {
+#pragma clang fp contract(off)
+  return x2 * c + x1 * s;
+}
+
+// Rotate the 8 dims d0 .. d0 + 7 (d0 a multiple of 8) of one row in place,
+// given the row's 8 partner dims (d0 + R/2, or d0 - R/2 in the second half)
+// and the row's table entry `cs` ([2][R/2] fp32: cos, then sin).  Dims past R
+// pass through.
+__device__ __forceinline__ void rope8(float (&x)[8], const float (&partner)[8], const float* cs, int d0, int rot) {
+  if (d0 >= rot) return;
+  const int half = rot / 2;
+  const bool first = d0 < half;
+  const int i0 = first ? d0 : d0 - half;
+  const f32x4 c0 = *reinterpret_cast<const f32x4*>(cs + i0);
+  const f32x4 c1 = *reinterpret_cast<const f32x4*>(cs + i0 + 4);
+  const f32x4 s0 = *reinterpret_cast<const f32x4*>(cs + half + i0);
+  const f32x4 s1 = *reinterpret_cast<const f32x4*>(cs + half + i0 + 4);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float co = i < 4 ? c0[i & 3] : c1[i & 3];
+    const float si = i < 4 ? s0[i & 3] : s1[i & 3];
+    x[i] = first ? rope_first(x[i], partner[i], co, si) : rope_second(partner[i], x[i], co, si);
+  }
+}
+
+// 8 source elements (fp16, or bf16 bit patterns) -> fp32, exactly
+__device__ __forceinline__ void src8_to_f32(const u32x4& r, bool bf, float (&x)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint16_t b = (uint16_t)(r[i >> 1] >> (16 * (i & 1)));
+    const float hv = (float)as<f16>(b), bv = bf16_to_f32(b);
+    x[i] = bf ? bv : hv;
+  }
+}
+
 // fp32 max |x| of a per-token INT8 row spread over `lanes` consecutive lanes
 // (a power of two; all of them active) holding 8 values each.
 __device__ __forceinline__ float row_absmax(const float (&x)[8], int lanes) {

@@ -120,6 +120,11 @@ struct AttnLaunch {
   int64_t new_v_stride;
   const int64_t* new_slots;  // [total_q] cache slot of each query token
   bool prefill;            // the prefill kernel takes the sequences prefill_sequence() selects
+  int64_t q_stride;        // elements between query tokens
+  const float* rope;       // RoPE table on the fused path, or nullptr
+  int32_t rope_max_pos;
+  int32_t rot;
+  const int64_t* positions;
 };
 
 // Rows of a (sequence, KV head) unit: g * q_len, in 16-row matrix-core tiles

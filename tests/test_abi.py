@@ -47,7 +47,7 @@ def test_exports_every_declared_symbol():
 
 def test_abi_version():
     L = _lib()
-    assert L.abi_version() == 4001
+    assert L.abi_version() == 5001
 
 
 @pytest.mark.parametrize("cname,pyname", [("ra_attn_args", "AttnArgs"), ("ra_qkv_rope_args", "RopeArgs")])
@@ -443,6 +443,31 @@ def test_fused_store_validation(kw, status, msg):
     lib = L.load_library()
     base = dict(new_k=FAKE, new_v=FAKE, new_dtype=L.RA_F16, new_k_stride=2 * 128, new_v_stride=2 * 128,
                 new_slots=FAKE)
+    base.update(kw)
+    a = _good_args(L, **base)
+    st = lib.ra_paged_attn(ctypes.byref(a), None)
+    assert st == status, (st, lib.ra_last_error())
+    assert msg in lib.ra_last_error().decode()
+
+
+BAD_ROPE_ATTN = [
+    (dict(new_k=None, new_v=None, new_slots=None), 1, "needs the fused store"),
+    (dict(positions=None), 1, "needs positions"),
+    (dict(rotary_dim=24), 1, "rotary_dim"),
+    (dict(rotary_dim=256), 1, "rotary_dim"),
+    (dict(rope_max_position=0), 1, "rope_max_position"),
+    (dict(rope_table=FAKE + 4), 3, "rope_table must be 16-byte aligned"),
+    (dict(q_token_stride=100), 1, "q_token_stride"),
+    (dict(q_token_stride=20 * 128 + 4), 3, "q_token_stride"),
+]
+
+
+@pytest.mark.parametrize("kw,status,msg", BAD_ROPE_ATTN, ids=[f"{i}-{m}" for i, (_, _, m) in enumerate(BAD_ROPE_ATTN)])
+def test_attention_rope_validation(kw, status, msg):
+    L = _lib()
+    lib = L.load_library()
+    base = dict(new_k=FAKE, new_v=FAKE, new_dtype=L.RA_F16, new_k_stride=20 * 128, new_v_stride=20 * 128,
+                new_slots=FAKE, rope_table=FAKE, rope_max_position=4096, rotary_dim=128, positions=FAKE)
     base.update(kw)
     a = _good_args(L, **base)
     st = lib.ra_paged_attn(ctypes.byref(a), None)

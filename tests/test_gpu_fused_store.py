@@ -144,3 +144,64 @@ def test_fused_store_graph_replay():
         assert torch.equal(kc, ref_k) and torch.equal(vc, ref_v), rep
     log("fused store: 3 graph replays equal to the eager launch")
     del g
+
+
+# name, ctx, q_len, Hq, Hkv, D, kv, src, rotary_dim, yarn factor, num_splits
+ROPE_CASES = [
+    ("verify_e4m3_yarn", [1000, 77, 513, 4097], 5, 16, 2, 128, "e4m3", "f16", 128, 2.0, 0),
+    ("decode_int8tok_d64_partial_bf16", [700, 33, 300], 1, 8, 2, 64, "int8_tok", "bf16", 32, 1.0, 2),
+    ("verify_f16_rot64_q3", [600, 200], 3, 16, 2, 128, "f16", "f16", 64, 4.0, 1),
+]
+
+
+@pytest.mark.parametrize("case", ROPE_CASES, ids=[c[0] for c in ROPE_CASES])
+def test_fused_rope_equals_qkv_rope_store_then_attention(case):
+    """RoPE on the fused path, with q, new_k and new_v as views into packed
+    QKV rows, against ra_qkv_rope_store followed by a plain ra_paged_attn:
+    caches (and scale planes), outputs and lse bit for bit.  A padding token
+    (slot -1) and a token whose position is outside the table are included."""
+    from oracle import rope as R
+    name, ctx, ql, hq, hkv, D, kv, src, rot, factor, S = case
+    pool = int(sum(-(-c // 16) for c in ctx) * 1.25) + 3
+    w = W.build(name, 53, ctx=ctx, q_len=ql, num_q_heads=hq, num_kv_heads=hkv, head_dim=D, kv_dtype=kv,
+                q_dtype=src, src_dtype=src, pool_pages=pool, num_splits=S)
+    new_rows = w.new_token_rows()
+    old_rows = np.setdiff1d(np.arange(w.tokens_k.shape[0]), new_rows)
+    pos, slots = W.step_positions_and_slots(w)
+    slots = slots.copy()
+    slots[1] = -1
+    max_pos = int(pos.max()) + 1
+    pos = pos.copy()
+    if len(pos) > 3:
+        pos[3] = max_pos               # outside the table: NaN rows, nothing stored
+    T = len(pos)
+    qkv = t_src(W.packed_qkv(53, T, hq, hkv, D, src, row_pad=8), src)
+    table = torch.from_numpy(R.rope_table(max_pos, rot, 1e6, factor, original_max=max(1, max_pos // 2))
+                             .astype(np.float32)).cuda()
+    q_view = qkv[:, :hq * D].view(T, hq, D)
+    k_view = qkv[:, hq * D:(hq + hkv) * D].view(T, hkv, D)
+    v_view = qkv[:, (hq + hkv) * D:(hq + 2 * hkv) * D].view(T, hkv, D)
+    pos_t = torch.from_numpy(pos).cuda()
+    slots_t = torch.from_numpy(slots).cuda()
+    bt = torch.from_numpy(w.block_tables).cuda()
+    cl = torch.from_numpy(w.ctx).cuda()
+    qsl = torch.from_numpy(w.query_start_loc).cuda()
+    common = dict(kv_dtype=kv, k_scale=w.k_scale, v_scale=w.v_scale, softmax_scale=w.softmax_scale,
+                  max_q_len=w.max_q_len, min_q_len=int(w.q_len.min()), max_context_len=w.max_context_len,
+                  num_splits=S)
+    # path A: one attention launch with the fused store and RoPE
+    kA, vA, ksA, vsA = _caches(w, old_rows)
+    oA, lA = P.paged_attn(q_view, kA, vA, bt, cl, qsl, k_scales=ksA, v_scales=vsA, new_k=k_view, new_v=v_view,
+                          new_slots=slots_t, rope_table=table, positions=pos_t, rotary_dim=rot, **common)
+    # path B: the fused QKV + RoPE + store kernel, then a plain attention
+    kB, vB, ksB, vsB = _caches(w, old_rows)
+    q_rot = P.qkv_rope_store(qkv, pos_t, table, slots_t, kB, vB, kv, num_q_heads=hq, rotary_dim=rot,
+                             k_scale=w.k_scale, v_scale=w.v_scale, k_scales=ksB, v_scales=vsB)
+    oB, lB = P.paged_attn(q_rot, kB, vB, bt, cl, qsl, k_scales=ksB, v_scales=vsB, **common)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(kA), _bits(kB)) and torch.equal(_bits(vA), _bits(vB)), f"{name}: caches differ"
+    if kv == "int8_tok":
+        assert torch.equal(_bits(ksA), _bits(ksB)) and torch.equal(_bits(vsA), _bits(vsB)), f"{name}: scales differ"
+    assert torch.equal(_bits(oA), _bits(oB)), f"{name}: outputs differ"
+    assert torch.equal(_bits(lA), _bits(lB)), f"{name}: lse differs"
+    log(f"{name}: RoPE + fused store in the attention launch == ra_qkv_rope_store + ra_paged_attn, bit for bit")
