@@ -96,12 +96,15 @@ __device__ __forceinline__ bool key_visible(const AttnLaunch& a, const SeqFrame&
 // prefix) share that XCD's L2.  With several row groups (long query blocks,
 // whose causal row groups differ in work) the ids stay in dispatch order, so
 // that the heaviest-first order below is spread evenly over the XCDs.
-// gridDim.x is a multiple of 8.
-__device__ __forceinline__ int64_t logical_block(int32_t row_groups) {
-  const int64_t bid = blockIdx.x;
+// The grid is padded_grid(units): a multiple of 8 below 2^31 (the host
+// rejects larger problems), so 32-bit arithmetic holds, and the per-XCD count
+// comes from the launch fields rather than from gridDim (which would cost a
+// dependent load of the dispatch packet before any other work).
+__device__ __forceinline__ uint32_t logical_block(uint32_t units, int32_t row_groups) {
+  const uint32_t bid = blockIdx.x;
   if (row_groups > 1) return bid;
-  const int64_t per_xcd = gridDim.x / 8;
-  return (bid % 8) * per_xcd + bid / 8;
+  const uint32_t per_xcd = (units + 7u) / 8u;
+  return (bid % 8u) * per_xcd + bid / 8u;
 }
 
 struct UnitId {
@@ -112,12 +115,12 @@ struct UnitId {
 // within a partition slot the last row group (the latest queries, which see
 // the most keys under the causal mask) comes first
 __device__ __forceinline__ bool decode_unit(const AttnLaunch& a, int32_t row_groups, UnitId& u) {
-  int64_t id = logical_block(row_groups);
-  const int64_t total = (int64_t)a.slots * a.hkv * row_groups * a.batch;
+  const uint32_t total = (uint32_t)a.slots * (uint32_t)a.hkv * (uint32_t)row_groups * (uint32_t)a.batch;
+  uint32_t id = logical_block(total, row_groups);
   if (id >= total) return false;
-  u.b = (int32_t)(id % a.batch); id /= a.batch;
-  u.h = (int32_t)(id % a.hkv); id /= a.hkv;
-  u.rg = row_groups - 1 - (int32_t)(id % row_groups); id /= row_groups;
+  u.b = (int32_t)(id % (uint32_t)a.batch); id /= (uint32_t)a.batch;
+  u.h = (int32_t)(id % (uint32_t)a.hkv); id /= (uint32_t)a.hkv;
+  u.rg = row_groups - 1 - (int32_t)(id % (uint32_t)row_groups); id /= (uint32_t)row_groups;
   u.s = (int32_t)id;
   return true;
 }

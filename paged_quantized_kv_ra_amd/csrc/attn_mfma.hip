@@ -443,6 +443,9 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
   // RoPE on the fused path: the workgroup's rotated query fragments, [nt][ks][lane]
   __shared__ f16x8 sm_q[NT][G::KS][kWave];
 
+  // one field of each 64-byte line of the launch arguments, so that the
+  // scalar loads of all of them are in flight together before the first branch
+  asm volatile("" ::"s"(a.q), "s"(a.batch), "s"(a.slots), "s"(a.kv_pos0), "s"(a.positions));
   UnitId u;
   if (!decode_unit(a, row_groups, u)) return;
   const int lane = threadIdx.x & 63;
@@ -450,7 +453,13 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
   const int kgrp = lane >> 4;
   const int ncol = lane & 15;
 
+  // the sequence's metadata in one round of loads (all four addresses are
+  // valid for any b < batch), before the first branch that depends on them
   const int32_t q0 = a.qsl[u.b], q1 = a.qsl[u.b + 1];
+  const int32_t ctx = a.context_lens[u.b];
+  const int32_t kv0 = a.kv_pos0 ? a.kv_pos0[u.b] : 0;
+  const int32_t qp0 = a.q_pos0 ? a.q_pos0[u.b] : 0;
+  asm volatile("" ::"v"(q0), "v"(q1), "v"(ctx), "v"(kv0), "v"(qp0));
   if (q0 < 0 || q1 < q0 || q1 > a.total_q) return;      // rows not addressable
   const int32_t g = a.hq / a.hkv;
   const int32_t q_len = q1 - q0;
@@ -458,10 +467,7 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
   if (rows == 0) return;
   const int32_t row0 = u.rg * kMfmaRowsPerBlock;
   if (row0 >= rows) return;
-  const int32_t ctx = a.context_lens[u.b];
   if (prefill_sequence(a, rows, ctx, q_len)) return;   // the prefill kernel's sequence
-  const int32_t kv0 = a.kv_pos0 ? a.kv_pos0[u.b] : 0;
-  const int32_t qp0 = a.q_pos0 ? a.q_pos0[u.b] : 0;
   bool bad = !seq_ok(a, ctx, q0, q1, kv0, qp0);
   const SeqFrame fr = seq_frame(a, ctx, q_len, kv0, qp0);
   // the row group's own queries i = row0 / g .. (last row) / g bound the keys
