@@ -151,17 +151,68 @@ __device__ __forceinline__ void wait_lgkmcnt0() {
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt at their maxima
 }
 
+// 32-bit LDS address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_u8*)p;
+}
+
+// The lane's 16-byte pieces of one ring slot: the K slabs, then the V slabs.
+// The reads are issued from inline assembly, each block waiting for its own
+// LDS returns (lgkmcnt(0)) before it ends.  The slot was written by LDS DMA,
+// which the compiler tracks only coarsely: for an ordinary LDS read of the
+// ring it would wait for every outstanding DMA (vmcnt(0)), including the
+// pages still in flight to the other slots, and the ring would stop
+// overlapping loads with arithmetic.  The caller's explicit vmcnt wait is the
+// one that retires this slot's loads.
 template <int KV, int D>
 __device__ __forceinline__ void read_page(PageRegs<KV, D>& r, const uint8_t (*ring)[kSlab], const float* scl,
                                           uint32_t lane_off, int kgrp) {
   using G = Geo<KV, D>;
-#pragma unroll
-  for (int j = 0; j < G::SLABS; ++j) r.k[j] = *reinterpret_cast<const u32x4*>(ring[j] + lane_off);
-#pragma unroll
-  for (int j = 0; j < G::SLABS; ++j) r.v[j] = *reinterpret_cast<const u32x4*>(ring[G::SLABS + j] + lane_off);
+  const uint32_t adr = lds_addr(ring[0]) + lane_off;
+  if constexpr (G::SLABS == 1) {
+    asm volatile(
+        "ds_read_b128 %0, %2\n\t"
+        "ds_read_b128 %1, %2 offset:1024\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r.k[0]), "=&v"(r.v[0])
+        : "v"(adr)
+        : "memory");
+  } else if constexpr (G::SLABS == 2) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %4 offset:1024\n\t"
+        "ds_read_b128 %2, %4 offset:2048\n\t"
+        "ds_read_b128 %3, %4 offset:3072\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r.k[0]), "=&v"(r.k[1]), "=&v"(r.v[0]), "=&v"(r.v[1])
+        : "v"(adr)
+        : "memory");
+  } else {
+    static_assert(G::SLABS == 4, "one, two or four 1 KiB slabs per page half");
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:1024\n\t"
+        "ds_read_b128 %2, %8 offset:2048\n\t"
+        "ds_read_b128 %3, %8 offset:3072\n\t"
+        "ds_read_b128 %4, %8 offset:4096\n\t"
+        "ds_read_b128 %5, %8 offset:5120\n\t"
+        "ds_read_b128 %6, %8 offset:6144\n\t"
+        "ds_read_b128 %7, %8 offset:7168\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r.k[0]), "=&v"(r.k[1]), "=&v"(r.k[2]), "=&v"(r.k[3]), "=&v"(r.v[0]), "=&v"(r.v[1]),
+          "=&v"(r.v[2]), "=&v"(r.v[3])
+        : "v"(adr)
+        : "memory");
+  }
   if constexpr (KV == KV_I8T) {
-    r.ks = *reinterpret_cast<const f32x4*>(scl + 4 * kgrp);
-    r.vs = *reinterpret_cast<const f32x4*>(scl + 16 + 4 * kgrp);
+    const uint32_t sadr = lds_addr(scl + 4 * kgrp);
+    asm volatile(
+        "ds_read_b128 %0, %2\n\t"
+        "ds_read_b128 %1, %2 offset:64\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r.ks), "=&v"(r.vs)
+        : "v"(sadr)
+        : "memory");
   }
 }
 
