@@ -380,7 +380,8 @@ int32_t ra_paged_attn_workspace(const ra_attn_args* args, int32_t* slots,
  * out = sum_s a_s out_s / sum_s a_s, lse = M + ln sum_s a_s, summed in the
  * order s = 0, 1, ...  out [rows][head_dim] of out_dtype (RA_F16, RA_BF16 or
  * RA_F32), lse_out [rows] fp32 or NULL.  head_dim in {64, 128};
- * num_partitions in [1, RA_KV_MAX_SPLITS]; 16-byte aligned buffers.
+ * num_partitions in [1, RA_KV_MAX_SPLITS]; rows in [0, 2^31 - 16];
+ * 16-byte aligned buffers.
  * (ReVolta README, "Quick start" and "Hardware": decode context parallelism
  * combines the partial attention of context parts.)
  */

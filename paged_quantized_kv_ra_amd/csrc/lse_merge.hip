@@ -10,9 +10,11 @@
 // nothing, whatever their out holds.  A NaN lse (a partial whose sequence
 // broke a precondition) makes the row NaN.
 //
-// One wavefront per row: lane s holds lse_s for a chunk of 64 partitions, the
+// One single-wave workgroup per row (rather than several rows per workgroup,
+// so that the launch spreads over every CU; about 1 us less per step on the
+// split workloads): lane s holds lse_s for a chunk of 64 partitions, the
 // weights are broadcast with a lane shuffle, each lane accumulates D/64 dims;
-// eight partial rows are in flight at a time.
+// sixteen partial rows are in flight at a time.
 #include "ra_device.h"
 #include "ra_internal.h"
 
@@ -20,12 +22,12 @@ namespace ra {
 namespace {
 
 template <int D, int OUT>
-__global__ void __launch_bounds__(256) lse_merge_kernel(MergeLaunch a) {
+__global__ void __launch_bounds__(64) lse_merge_kernel(MergeLaunch a) {
   constexpr int PER = D / 64;
   constexpr int BATCH = 16;                    // partial rows in flight per lane
   // every launch argument in one round of scalar loads, ahead of the first branch
   asm volatile("" ::"s"(a.part_out), "s"(a.part_lse), "s"(a.parts), "s"(a.rows), "s"(a.out), "s"(a.lse));
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t row = blockIdx.x;
   if (row >= a.rows) return;
   const int lane = threadIdx.x & 63;
   const float* base_o = a.part_out + row * D + lane * PER;
@@ -118,7 +120,7 @@ __global__ void __launch_bounds__(256) lse_merge_kernel(MergeLaunch a) {
 
 template <int D>
 hipError_t launch_out(const MergeLaunch& a, hipStream_t s) {
-  const dim3 g((unsigned)((a.rows + 3) / 4)), b(256);
+  const dim3 g((unsigned)a.rows), b(64);
   switch (a.out_dtype) {
     case 1: hipLaunchKernelGGL((lse_merge_kernel<D, 1>), g, b, 0, s, a); break;
     case 2: hipLaunchKernelGGL((lse_merge_kernel<D, 2>), g, b, 0, s, a); break;

@@ -134,6 +134,9 @@ int32_t check_attn(const ra_attn_args* a, Plan* plan) {
   }
   plan->direct = plan->slots == 1 && a->out != nullptr;
 
+  // the merge launches one workgroup per query row
+  if ((int64_t)a->total_q * a->num_q_heads > (int64_t)0x7FFFFFF0)
+    return fail(RA_ERR_INVALID_ARG, "ra_paged_attn: total_q * num_q_heads above 2^31 - 16");
   // grid size: slots * Hkv * row groups * batch blocks
   const int64_t rg = ceil_div(rows_max, ra::kMfmaRowsPerBlock);
   if ((int64_t)plan->slots * a->num_kv_heads * rg * a->batch > (int64_t)0x7FFFFFF0)
@@ -381,7 +384,7 @@ int32_t ra_lse_merge(const float* partial_out, const float* partial_lse, int32_t
   if (out_dtype != RA_F16 && out_dtype != RA_BF16 && out_dtype != RA_F32)
     return fail(RA_ERR_UNSUPPORTED, "ra_lse_merge: out_dtype %d unknown", out_dtype);
   if (rows == 0) return RA_OK;
-  if (rows > (int64_t)0x7FFFFFF0 * 4) return fail(RA_ERR_INVALID_ARG, "ra_lse_merge: too many rows");
+  if (rows > (int64_t)0x7FFFFFF0) return fail(RA_ERR_INVALID_ARG, "ra_lse_merge: too many rows");   // one workgroup per row
   if (!partial_out || !partial_lse || !out)
     return fail(RA_ERR_INVALID_ARG, "ra_lse_merge: partial_out, partial_lse and out must be non-NULL");
   if (!aligned16(partial_out) || !aligned16(out))

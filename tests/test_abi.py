@@ -150,6 +150,8 @@ BAD_ATTN = [
     (dict(num_splits=4, partial_out=FAKE, partial_lse=FAKE, partial_slots=3), 4, "slots"),
     (dict(num_splits=4, partial_out=FAKE + 4, partial_lse=FAKE, partial_slots=4), 3, "partial_out"),
     (dict(out=0, num_splits=1), 4, "out is NULL"),
+    # the merge launches one workgroup per query row: total_q * num_q_heads <= 2^31 - 16
+    (dict(total_q=(0x7FFFFFF0 // 16) + 1, max_q_len=(0x7FFFFFF0 // 16) + 1), 1, "total_q * num_q_heads"),
 ]
 
 
@@ -242,6 +244,7 @@ def test_store_zero_tokens_ok_and_fp16_ignores_scale():
     ((FAKE, FAKE, 0, 10, 128, FAKE, 1, FAKE), 1, "num_partitions"),
     ((FAKE, FAKE, 5000, 10, 128, FAKE, 1, FAKE), 1, "num_partitions"),
     ((FAKE, FAKE, 2, -1, 128, FAKE, 1, FAKE), 1, "rows"),
+    ((FAKE, FAKE, 2, 0x7FFFFFF0 + 1, 128, FAKE, 1, FAKE), 1, "too many rows"),
     ((FAKE, FAKE, 2, 10, 80, FAKE, 1, FAKE), 2, "head_dim"),
     ((FAKE, FAKE, 2, 10, 128, FAKE, 7, FAKE), 2, "out_dtype"),
     ((0, FAKE, 2, 10, 128, FAKE, 1, FAKE), 1, "non-NULL"),
