@@ -51,8 +51,12 @@ temperature factor; position 0 is the identity; q.k after rotation depends
 only on the position difference; plain RoPE matches a hand-worked value;
 YaRN keeps the highest frequencies, divides the lowest by the factor (so
 that the table at position 2p equals plain RoPE at p there), blends
-monotonically in between and gives the temperature 1.0693...; the fused
-step at position 0 without scaling reproduces the plain store and Q.
+monotonically in between and gives the temperature 1.0693...; YaRN
+frequencies and temperature equal, on every dim including both ramp ends,
+those of the Hugging Face runtime's own YaRN parameter function for the same
+config entry (a library routine that applies the format the pages name), and
+a ramp end moved by one dim would differ from it; the fused step at position
+0 without scaling reproduces the plain store and Q.
 """
 import math
 

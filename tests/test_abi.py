@@ -417,6 +417,38 @@ def test_rope_table_matches_oracle(max_pos, rot, base, factor, orig):
     assert np.mean(got == want.astype(np.float32)) > 0.999
 
 
+@pytest.mark.parametrize("rot,head_dim,base,orig,factor", [
+    (128, 128, 1e6, 262144, 2.0),     # the pages' deployment: YaRN factor 2 over 262,144 positions
+    (128, 128, 1e4, 4096, 2.0),
+    (64, 64, 1e4, 2048, 4.0),
+    (64, 128, 1e6, 32768, 2.0),       # partial rotary
+    (16, 64, 500.0, 100, 2.0),
+])
+def test_rope_table_matches_the_runtime_yarn_routine(rot, head_dim, base, orig, factor):
+    """The library's table pinned to a library routine, independently of the
+    oracle: at position 1 each pair's angle is its frequency and its length the
+    attention temperature; both must equal what the Hugging Face runtime's YaRN
+    function gives for the same config entry, on every dim (ramp ends
+    included)."""
+    import numpy as np
+    transformers = pytest.importorskip("transformers")
+    from transformers.modeling_rope_utils import _compute_yarn_parameters
+    cfg = transformers.PretrainedConfig()
+    cfg.hidden_size, cfg.num_attention_heads, cfg.head_dim = head_dim * 4, 4, head_dim
+    cfg.max_position_embeddings = int(orig * factor)
+    cfg.rope_parameters = {"rope_type": "yarn", "rope_theta": base, "factor": factor,
+                           "original_max_position_embeddings": orig, "partial_rotary_factor": rot / head_dim}
+    inv, m = _compute_yarn_parameters(cfg, "cpu")
+    inv = inv.double().numpy()
+    L = _lib()
+    t = L.rope_table(2, rot, base, factor, orig, device=None).numpy().astype(np.float64)
+    freq = np.arctan2(t[1, 1], t[1, 0])
+    np.testing.assert_allclose(freq, inv, rtol=3e-6, atol=0)
+    np.testing.assert_allclose(np.hypot(t[1, 0], t[1, 1]), float(m), rtol=1e-6)
+    np.testing.assert_allclose(t[0, 0], float(m), rtol=1e-7)
+    assert np.all(t[0, 1] == 0.0)
+
+
 def test_rope_table_validation():
     L = _lib()
     lib = L.load_library()

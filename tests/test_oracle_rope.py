@@ -187,3 +187,66 @@ def test_fused_step_position_out_of_table():
     assert np.isnan(q_out[0].astype(np.float32)).all() and np.isfinite(q_out[1].astype(np.float32)).all()
     k = OL.gather(kc, np.array([0, 1]), "k", hkv, D, "e4m3")
     assert np.all(k[0] == 0x7F) and not np.all(k[1] == 0x7F)
+
+
+# ---------------------------------------------------------------------------
+# YaRN against a library routine: the Hugging Face runtime's own YaRN
+# parameter function (transformers.modeling_rope_utils), which applies the
+# config entry the pages give ("Quick start", step 2: rope_type yarn, factor
+# 2, original_max_position_embeddings 262144).  Every dim is compared,
+# including both ends of the ramp, so a floor / ceil or truncation slip at
+# either end fails.  The routine computes in fp32, hence the 2e-6 tolerance;
+# moving a ramp end by one dim changes some frequency by far more.
+
+YARN_CASES = [
+    # (rotary_dim, head_dim, base, original_max, factor)
+    (128, 128, 1e6, 262144, 2.0),     # the pages' deployment (rope base is a parameter)
+    (128, 128, 1e4, 262144, 2.0),
+    (128, 128, 1e4, 4096, 2.0),
+    (64, 64, 1e4, 2048, 4.0),
+    (128, 128, 5e5, 8192, 8.0),
+    (64, 128, 1e6, 32768, 2.0),       # partial rotary: 64 of 128 dims
+    (16, 64, 500.0, 100, 2.0),        # short ramp clamped at both ends
+]
+
+
+def _hf_yarn(rot, head_dim, base, orig, factor):
+    transformers = pytest.importorskip("transformers")
+    from transformers.modeling_rope_utils import _compute_yarn_parameters
+    cfg = transformers.PretrainedConfig()
+    cfg.hidden_size = head_dim * 4
+    cfg.num_attention_heads = 4
+    cfg.head_dim = head_dim
+    cfg.max_position_embeddings = int(orig * factor)
+    cfg.rope_parameters = {"rope_type": "yarn", "rope_theta": base, "factor": factor,
+                           "original_max_position_embeddings": orig,
+                           "partial_rotary_factor": rot / head_dim}
+    inv, attention_factor = _compute_yarn_parameters(cfg, "cpu")
+    return inv.double().numpy(), float(attention_factor)
+
+
+@pytest.mark.parametrize("rot,head_dim,base,orig,factor", YARN_CASES)
+def test_yarn_matches_the_runtime_routine_on_every_dim(rot, head_dim, base, orig, factor):
+    want, m = _hf_yarn(rot, head_dim, base, orig, factor)
+    got = R.yarn_inv_freq(rot, base, factor, orig)
+    assert got.shape == want.shape
+    np.testing.assert_allclose(got, want, rtol=2e-6, atol=0)
+    assert abs(R.yarn_temperature(factor) - m) < 1e-12
+
+
+@pytest.mark.parametrize("rot,head_dim,base,orig,factor", YARN_CASES[:5])
+def test_yarn_ramp_end_slips_are_caught(rot, head_dim, base, orig, factor):
+    """The comparison above has the power to see a ramp end moved by one dim:
+    the frequencies with either end shifted differ from the routine's by far
+    more than its tolerance."""
+    want, _ = _hf_yarn(rot, head_dim, base, orig, factor)
+    theta = R.inv_freq(rot, base)
+    lo = max(math.floor(R.yarn_correction_dim(rot, base, orig, 32.0)), 0)
+    hi = min(math.ceil(R.yarn_correction_dim(rot, base, orig, 1.0)), rot - 1)
+    d = np.arange(rot // 2, dtype=np.float64)
+    for l2, h2 in ((lo + 1, hi), (lo - 1, hi), (lo, hi + 1), (lo, hi - 1)):
+        if l2 < 0 or h2 <= l2:
+            continue
+        ramp = np.clip((d - l2) / (h2 - l2), 0.0, 1.0)
+        slipped = theta * (1.0 - ramp) + theta / factor * ramp
+        assert np.max(np.abs(slipped - want) / want) > 1e-3, (l2, h2)
