@@ -26,13 +26,17 @@ head h reads KV head h // (Hq / Hkv).  Key j is visible to query i iff
 j <= pos_i and (W < 0 or pos_i - j < W or j < n_sink).  Then
     s_j = softmax_scale * q_i . k_j,   m = max s_j,   l = sum exp(s_j - m),
     out = sum exp(s_j - m) v_j / l,    lse = m + ln l      (natural log).
-A query with no visible key gets out = 0 and lse = -inf.
+A query with no visible key gets out = 0 and lse = -inf.  The arithmetic is
+IEEE's: a NaN score (a NaN in q or in a visible key) makes m, and with it
+out and lse, NaN for that query; a NaN in a visible value makes out NaN.
 
 Split-KV: partition s of a sequence covers keys [s*P, min((s+1)*P, ctx));
 with an explicit count S, P = 16 * ceil(ceil(ctx / S) / 16).  Each
 partition yields (out_s, lse_s) as above restricted to its keys.  Merge:
 M = max lse_s; if M = -inf the result is (0, -inf); else
-a_s = exp(lse_s - M), out = sum a_s out_s / sum a_s, lse = M + ln sum a_s.
+a_s = exp(lse_s - M), out = sum a_s out_s / sum a_s, lse = M + ln sum a_s
+(a NaN lse_s makes the row NaN; an empty partition, lse_s = -inf, adds
+nothing whatever its out holds).
 
 Pins (tests/test_oracle_attention.py): torch scaled_dot_product_attention
 in float64 on the CPU with an explicit boolean mask and repeated KV heads;
@@ -40,7 +44,10 @@ a brute-force np.longdouble formulation without max subtraction on tiny
 cases; a hand-computed closed-form case; uniform-V, identical-key,
 single-key and dominant-key invariants; window >= ctx equals plain causal;
 token permutation invariance; merge(split(S)) equals unsplit for several S
-including empty partitions; merge associativity; S = 1 identity.
+including empty partitions; merge associativity; S = 1 identity; NaN in a
+query row, a visible key or a visible value propagates under IEEE
+arithmetic to exactly the rows that see it, and a NaN partial lse poisons
+its merged row.
 """
 import math
 
@@ -97,12 +104,16 @@ def attention(q, k, v, softmax_scale, window_left=-1, num_sinks=0,
         s = softmax_scale * (qh @ kh.T)                       # [q_len*g, n]
         mask = np.repeat(vis_c, g, axis=0)
         s = np.where(mask, s, -np.inf)
-        m = s.max(axis=1)
-        has = np.isfinite(m)
+        m = s.max(axis=1)                                     # NaN if any visible score is NaN
+        has = m != -np.inf                                    # no visible key: m = -inf
         w = np.where(mask, np.exp(s - np.where(has, m, 0.0)[:, None]), 0.0)
         l = w.sum(axis=1)
         o = np.zeros((q_len * g, dim))
-        o[has] = (w[has] @ vh) / l[has][:, None]
+        if np.isfinite(vh).all():
+            o[has] = (w[has] @ vh) / l[has][:, None]
+        else:   # sum over each row's visible keys only, so that 0 * NaN never enters
+            for r in np.nonzero(has)[0]:
+                o[r] = (w[r, mask[r]] @ vh[mask[r]]) / l[r]
         ls = np.full(q_len * g, -np.inf)
         ls[has] = m[has] + np.log(l[has])
         out[:, h * g:(h + 1) * g, :] = o.reshape(q_len, g, dim)
@@ -141,11 +152,12 @@ def lse_merge(partial_out, partial_lse):
     """Merge partials along axis 0: returns (out, lse) in float64."""
     po = np.asarray(partial_out, dtype=np.float64)
     pl = np.asarray(partial_lse, dtype=np.float64)
-    m = pl.max(axis=0)
-    has = np.isfinite(m)
-    a = np.where(np.isfinite(pl), np.exp(pl - np.where(has, m, 0.0)), 0.0)
+    m = pl.max(axis=0)                                        # NaN if any lse_s is NaN
+    has = m != -np.inf                                        # every partition empty: m = -inf
+    live = pl != -np.inf                                      # empty partitions add nothing
+    a = np.where(live, np.exp(pl - np.where(has, m, 0.0)), 0.0)
     den = a.sum(axis=0)
-    num = (a[..., None] * np.where(np.isfinite(pl)[..., None], po, 0.0)).sum(axis=0)
+    num = (a[..., None] * np.where(live[..., None], po, 0.0)).sum(axis=0)
     out = np.where(has[..., None], num / np.where(has, den, 1.0)[..., None], 0.0)
     lse = np.where(has, m + np.log(np.where(has, den, 1.0)), -np.inf)
     return out, lse

@@ -296,3 +296,80 @@ def test_explicit_positions_match_brute_force():
                 want = (e[:, None] * v[keys, 0]).sum(axis=0) / e.sum()
                 np.testing.assert_allclose(o[i, h], want, rtol=1e-12, atol=1e-14)
                 assert abs(l[i, h] - (m + np.log(e.sum()))) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# NaN inputs: the definition evaluated in IEEE arithmetic.  A NaN score makes
+# the row's maximum NaN (IEEE maximum propagates it), so the row's out and lse
+# are NaN; a NaN value makes out NaN (lse does not depend on V); rows that do
+# not see the NaN key or value are unchanged.
+
+def _nan_case(seed=7):
+    rng = np.random.default_rng(seed)
+    ctx, ql, hq, hkv, D = 40, 4, 4, 2, 16
+    q = rng.standard_normal((ql, hq, D))
+    k = rng.standard_normal((ctx, hkv, D))
+    v = rng.standard_normal((ctx, hkv, D))
+    return q, k, v, 0.25
+
+
+def test_nan_query_row_is_nan_and_others_unchanged():
+    q, k, v, sc = _nan_case()
+    ref_o, ref_l = A.attention(q, k, v, sc)
+    q2 = q.copy()
+    q2[2, 1, 5] = np.nan                      # query 2, head 1
+    o, l = A.attention(q2, k, v, sc)
+    assert np.isnan(o[2, 1]).all() and np.isnan(l[2, 1])
+    keep = np.ones(o.shape[:2], bool)
+    keep[2, 1] = False
+    assert np.array_equal(o[keep], ref_o[keep]) and np.array_equal(l[keep], ref_l[keep])
+
+
+def test_nan_key_poisons_exactly_the_queries_that_see_it():
+    q, k, v, sc = _nan_case()
+    ref_o, ref_l = A.attention(q, k, v, sc)
+    ctx, ql = k.shape[0], q.shape[0]
+    j = ctx - ql + 2                          # visible to queries 2, 3 only (causal)
+    k2 = k.copy()
+    k2[j, 0, 3] = np.nan                      # KV head 0 = query heads 0, 1
+    o, l = A.attention(q, k2, v, sc)
+    for i in range(ql):
+        for h in range(q.shape[1]):
+            if i >= 2 and h < 2:
+                assert np.isnan(o[i, h]).all() and np.isnan(l[i, h])
+            else:
+                assert np.array_equal(o[i, h], ref_o[i, h]) and l[i, h] == ref_l[i, h]
+
+
+def test_nan_value_poisons_out_of_the_queries_that_see_it_only():
+    q, k, v, sc = _nan_case()
+    ref_o, ref_l = A.attention(q, k, v, sc)
+    ctx, ql = k.shape[0], q.shape[0]
+    j = ctx - 1                               # visible to the last query only
+    v2 = v.copy()
+    v2[j, 1, 7] = np.nan                      # KV head 1 = query heads 2, 3; dim 7
+    o, l = A.attention(q, k, v2, sc)
+    assert np.array_equal(l, ref_l)           # lse does not depend on V
+    for i in range(ql):
+        for h in range(q.shape[1]):
+            # (a value that is not finite takes the oracle's row-by-row sum, which
+            # may round differently from the matrix product in the last bit)
+            if i == ql - 1 and h >= 2:
+                assert np.isnan(o[i, h, 7])
+                np.testing.assert_allclose(np.delete(o[i, h], 7), np.delete(ref_o[i, h], 7), rtol=1e-13, atol=0)
+            else:
+                np.testing.assert_allclose(o[i, h], ref_o[i, h], rtol=1e-13, atol=0)
+
+
+def test_nan_partial_lse_poisons_its_merged_row():
+    rng = np.random.default_rng(8)
+    po = rng.standard_normal((3, 5, 8))
+    pl = rng.standard_normal((3, 5))
+    pl[1, 0] = -np.inf                        # an empty partition: contributes nothing
+    po[1, 0] = np.nan                         # ... whatever its out holds
+    pl[2, 3] = np.nan
+    o, l = A.lse_merge(po, pl)
+    assert np.isnan(o[3]).all() and np.isnan(l[3])
+    ref = A.lse_merge(po[[0, 2]][:, [0]], pl[[0, 2]][:, [0]])
+    np.testing.assert_allclose(o[0], ref[0][0], rtol=1e-15)
+    assert np.isfinite(o[[0, 1, 2, 4]]).all() and np.isfinite(l[[0, 1, 2, 4]]).all()
