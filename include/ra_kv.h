@@ -88,7 +88,7 @@
 extern "C" {
 #endif
 
-#define RA_KV_ABI_VERSION 5
+#define RA_KV_ABI_VERSION 6
 #define RA_KV_LAYOUT_ID 1
 #define RA_KV_PAGE_SIZE 16
 #define RA_KV_MAX_SPLITS 4096
@@ -269,7 +269,13 @@ int32_t ra_qkv_rope_store(const ra_qkv_rope_args* args, void* stream);
  * new_k and new_v is the K and V of query token q, slot new_slots[q]; slot
  * < 0 or >= num_pages * 16 stores nothing), each token stored by the
  * workgroups of the partition holding its position, before they read it; the
- * separate ra_kv_store call and its launch go away.  The slot of query i of
+ * separate ra_kv_store call and its launch go away.  The fused store WRITES
+ * k_cache and v_cache (and, for RA_KV_INT8_TOKEN, k_scales and v_scales) at
+ * the new tokens' slots; without new_k the launch only reads them.  A page
+ * that receives a new token must be read by no other sequence of the same
+ * launch (a partly filled page shared between sequences through prefix
+ * caching must not take new tokens): the other sequence's workgroups could
+ * read it before or after the store.  The slot of query i of
  * sequence b must be the block table's slot for its position p (local to this
  * cache): block_tables[b][p / 16] * 16 + p % 16.  Tokens whose position lies
  * outside [0, ctx_b) are not stored (they belong to another context-parallel
@@ -299,8 +305,8 @@ typedef struct ra_attn_args {
   const void* q;                   /* [total_q][num_q_heads][head_dim]           */
   void* out;                       /* [total_q][num_q_heads][head_dim] or NULL   */
   float* lse;                      /* [total_q][num_q_heads] or NULL             */
-  const void* k_cache;             /* paged layout above                         */
-  const void* v_cache;
+  void* k_cache;                   /* paged layout above; read, and written by   */
+  void* v_cache;                   /* the fused store (see above)                */
   int32_t kv_dtype;                /* RA_KV_*                                    */
   float k_scale;                   /* (host) > 0, finite for E4M3 / INT8         */
   float v_scale;
@@ -325,8 +331,9 @@ typedef struct ra_attn_args {
   float* partial_out;              /* workspace, see above                       */
   float* partial_lse;
   int32_t partial_slots;           /* slots the partial buffers hold             */
-  const float* k_scales;           /* RA_KV_INT8_TOKEN: scale planes (layout     */
-  const float* v_scales;           /* above); ignored by the other formats       */
+  float* k_scales;                 /* RA_KV_INT8_TOKEN: scale planes (layout     */
+  float* v_scales;                 /* above; written by the fused store too);    */
+                                   /* ignored by the other formats               */
   const int32_t* kv_pos0;          /* [batch] or NULL: global position of key 0  */
   const int32_t* q_pos0;           /* [batch] or NULL: global position of query 0*/
   /* Fused store (decode and verify): the query tokens' own K/V rows, stored

@@ -267,7 +267,42 @@ struct Acc {
   float m[NT];
   float mc[NT];   // c * m, or 0 while m = -inf: the rows' exponent offset
   float l[NT];    // the lane's partial row sums (per-token INT8)
+  // Per-token INT8: the V scales ride on P relative to a power-of-two
+  // reference vref (wave-uniform), so that the fp16 operand p * vs / vref
+  // stays in fp16's normal range whatever the magnitude of V: every V scale
+  // seen is at most 2^7 vref, hence p * vs / vref <= 2^8 * 2^7, and O
+  // holds sums in units of vref.  0 until the first non-zero scale.
+  float vref, vinv;
 };
+
+// Per-token INT8: take up a page's V scales into the wave's power-of-two
+// reference.  When a scale exceeds 2^7 vref the reference moves to 2^(e - 7) for
+// the page's largest scale f * 2^e (f in [0.5, 1)), and what was accumulated
+// in units of the old reference (O, and the pending page's probabilities) is
+// rescaled exactly by the ratio of the two powers of two.
+template <int KV, int D, int NT>
+__device__ __forceinline__ void take_v_scales(Acc<KV, D, NT>& acc, const f32x4& vs, float (&pend)[NT][4]) {
+  float vm = fmaxf(fmaxf(vs[0], vs[1]), fmaxf(vs[2], vs[3]));
+  vm = fmaxf(vm, __shfl_xor(vm, 16));   // the lanes' token quads: kgrp = lane bits 4, 5
+  vm = fmaxf(vm, __shfl_xor(vm, 32));
+  vm = __builtin_amdgcn_readfirstlane(vm);
+  if (vm > acc.vref * 128.0f) {
+    int32_t e = (int32_t)((__float_as_uint(vm) >> 23) & 0xFFu) - 126;   // vm = f * 2^e, f in [0.5, 1)
+    e = min(max(e, -119), 120);                                         // vref and 1 / vref stay normal
+    const float nref = __uint_as_float((uint32_t)(e - 7 + 127) << 23);
+    const float ninv = __uint_as_float((uint32_t)(7 - e + 127) << 23);
+    const float f = acc.vref * ninv;                                    // old / new: a power of two, or 0
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+      for (int mt = 0; mt < Geo<KV, D>::MT; ++mt) acc.o[mt][nt] *= f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pend[nt][i] *= f;
+    }
+    acc.vref = nref;
+    acc.vinv = ninv;
+  }
+}
 
 // QK, masks and the online softmax of one page.  p receives the page's
 // unnormalised probabilities (times the per-token V scales for per-token
@@ -327,6 +362,9 @@ __device__ __forceinline__ void scores_softmax(Acc<KV, D, NT>& acc, PageRegs<KV,
         for (int i = 0; i < 4; ++i) pend[nt][i] *= alpha;
       }
     }
+    float vsn[4];   // per-token INT8: the V scales in units of the reference
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vsn[i] = KV == KV_I8T ? r.vs[i] * acc.vinv : 1.0f;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       float ps = 0.0f;
@@ -334,7 +372,7 @@ __device__ __forceinline__ void scores_softmax(Acc<KV, D, NT>& acc, PageRegs<KV,
       for (int i = 0; i < 4; ++i) {
         const float e = __builtin_amdgcn_exp2f(fmaf(s[nt][i], c, -acc.mc[nt]));
         if constexpr (!kOnesSum<KV>) ps += e;
-        p[nt][i] = KV == KV_I8T ? e * r.vs[i] : e;   // per-token V scales ride on P
+        p[nt][i] = KV == KV_I8T ? e * vsn[i] : e;   // per-token V scales ride on P
       }
       if constexpr (!kOnesSum<KV>) acc.l[nt] += ps;
     }
@@ -361,6 +399,7 @@ __device__ __forceinline__ void scores_softmax(Acc<KV, D, NT>& acc, PageRegs<KV,
 #pragma unroll
       for (int w = 0; w < 4; ++w) r.v[sl][w] &= KV == KV_F16 ? ((w & 1) ? keep_hi : keep_lo) : keep8;
   }
+  if constexpr (KV == KV_I8T) take_v_scales<KV, D, NT>(acc, r.vs, pend);
   softmax();
 }
 
@@ -409,10 +448,9 @@ __device__ __forceinline__ bool store_new_tokens(const AttnLaunch& a, int h, int
         const int64_t page = slot >> 4;
         const int tp = (int)(slot & 15);
         if constexpr (KV == KV_I8T) {
-          if (c == 0) const_cast<float*>(is_v ? a.v_scales : a.k_scales)[(page * a.hkv + h) * kPage + tp] = sc;
+          if (c == 0) (is_v ? a.v_scales : a.k_scales)[(page * a.hkv + h) * kPage + tp] = sc;
         }
-        // the caches and scale planes are the caller's writable buffers (read-only to the attention itself)
-        uint8_t* blk = const_cast<uint8_t*>(is_v ? a.v_cache : a.k_cache) + (page * a.hkv + h) * (int64_t)(kPage * D * E);
+        uint8_t* blk = (is_v ? a.v_cache : a.k_cache) + (page * a.hkv + h) * (int64_t)(kPage * D * E);
         store_row8<KV, D>(blk, tp, 8 * c, x, sc, is_v);
       }
     }
@@ -651,6 +689,7 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
 #pragma unroll
     for (int mt = 0; mt < G::MT; ++mt) acc.o[mt][nt] = f32x4{0, 0, 0, 0};
   }
+  acc.vref = acc.vinv = 0.0f;
   const float c = a.softmax_scale * a.k_scale * kLog2e;
   const float thr = kLazy / c;
 
@@ -766,6 +805,7 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
     }
     Mrow[nt] = M;
     Lrow[nt] = L;
+    if constexpr (KV == KV_I8T) fself[nt] *= acc.vref;   // O back from units of the wave's reference
   }
 
   // ---- reduce-scatter of O through LDS, in two passes over the lane's
@@ -814,7 +854,9 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
       if (r < rows) {
         const int32_t qi = r / g, hj = r % g;
         const int64_t orow = (int64_t)(q0 + qi) * a.hq + u.h * g + hj;
-        const float inv = L > 0.0f ? vs / L : 0.0f;
+        // a row with no visible key has L = 0 (out 0, lse -inf); NaN scores
+        // leave L = NaN, and the row stays NaN in out and lse
+        const float inv = L > 0.0f ? vs / L : (L == L ? 0.0f : __builtin_nanf(""));
         const int d0 = (4 * kgrp + i) * G::MT;
 #pragma unroll
         for (int mt = 0; mt < G::MT; ++mt) v[mt] = bad ? __builtin_nanf("") : v[mt] * inv;
@@ -843,7 +885,7 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
             *reinterpret_cast<f32x4*>(op + 4 * k) = f32x4{v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]};
         }
         if (kgrp == 0 && i == 0) {
-          float lse = L > 0.0f ? (M * c + log2f(L)) * kLn2 : -INFINITY;
+          float lse = L > 0.0f ? (M * c + log2f(L)) * kLn2 : (L == L ? -INFINITY : __builtin_nanf(""));
           if (bad) lse = __builtin_nanf("");
           if (a.direct) {
             if (a.lse) a.lse[orow] = lse;

@@ -292,7 +292,7 @@ __global__ void __launch_bounds__(kPThreads) attn_prefill_kernel(AttnLaunch a, i
     const int32_t qi = r / g, hj = r % g;
     const int64_t orow = (int64_t)(q0 + qi) * a.hq + h * g + hj;
     const float L = ls[nt][0];
-    const float inv = L > 0.0f ? vs / L : 0.0f;
+    const float inv = L > 0.0f ? vs / L : (L == L ? 0.0f : __builtin_nanf(""));   // NaN scores: NaN row
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float v[kPMT];
@@ -315,7 +315,7 @@ __global__ void __launch_bounds__(kPThreads) attn_prefill_kernel(AttnLaunch a, i
       }
     }
     if (kgrp == 0) {
-      float lse = L > 0.0f ? (m[nt] * c + log2f(L)) * kPLn2 : -INFINITY;
+      float lse = L > 0.0f ? (m[nt] * c + log2f(L)) * kPLn2 : (L == L ? -INFINITY : __builtin_nanf(""));
       if (bad) lse = __builtin_nanf("");
       if (a.direct) {
         if (a.lse) a.lse[orow] = lse;

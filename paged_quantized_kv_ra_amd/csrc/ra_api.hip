@@ -222,8 +222,8 @@ ra::AttnLaunch make_launch(const ra_attn_args* a, const Plan& p) {
   L.lse = p.direct ? a->lse : nullptr;
   L.part_out = a->partial_out;
   L.part_lse = a->partial_lse;
-  L.k_cache = static_cast<const uint8_t*>(a->k_cache);
-  L.v_cache = static_cast<const uint8_t*>(a->v_cache);
+  L.k_cache = static_cast<uint8_t*>(a->k_cache);
+  L.v_cache = static_cast<uint8_t*>(a->v_cache);
   L.kv = kv_kind(a->kv_dtype);
   const bool quant = per_layer_scales(a->kv_dtype);
   L.k_scale = quant ? a->k_scale : 1.0f;

@@ -82,8 +82,8 @@ struct AttnLaunch {
   float* lse;            // final lse (direct write) or nullptr
   float* part_out;       // [slots][total_q][Hq][D] when slots > 1 or out == nullptr
   float* part_lse;       // [slots][total_q][Hq]
-  const uint8_t* k_cache;
-  const uint8_t* v_cache;
+  uint8_t* k_cache;      // read; written by the fused store
+  uint8_t* v_cache;
   int kv;                // KvKind
   float k_scale;         // 1 for FP16 caches
   float v_scale;
@@ -108,8 +108,8 @@ struct AttnLaunch {
   int32_t part_tokens;   // auto mode: partition size (tokens) of units with >= kSmallUnitRows rows
   int32_t part_small;    // auto mode: partition size of units with fewer rows
   bool direct;           // write out/lse directly (one slot)
-  const float* k_scales; // KV_I8T scale planes [num_pages][hkv][16]
-  const float* v_scales;
+  float* k_scales;       // KV_I8T scale planes [num_pages][hkv][16] (written by the fused store)
+  float* v_scales;
   const int32_t* kv_pos0;  // [batch] global position of cache key 0, or nullptr (0)
   const int32_t* q_pos0;   // [batch] global position of the block's first query, or nullptr
   // fused store of the query tokens' own K/V rows (nullptr: none)

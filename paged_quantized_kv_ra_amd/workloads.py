@@ -40,13 +40,24 @@ def f32_to_bf16_bits(x):
     return r.astype(np.uint16)
 
 
-def _normal(rng, shape, out_dtype):
-    """Draw fp32 N(0,1) of ``shape`` in chunks and cast to ``out_dtype``."""
+def _normal(rng, shape, out_dtype, std=1.0):
+    """Draw fp32 N(0, std^2) of ``shape`` in chunks (N(0,1) draws times std in
+    fp32) and cast to ``out_dtype``.  ``std`` is a scalar, or one value per
+    index of the first axis (a per-token magnitude)."""
     n = int(np.prod(shape))
     flat = np.empty(n, dtype=np.float16 if out_dtype == "f16" else np.uint16)
+    std = np.asarray(std, dtype=np.float32)
+    per_row = std.ndim > 0
+    if per_row:
+        assert std.shape == (shape[0],)
+        inner = n // shape[0] if shape[0] else 1
     for lo in range(0, n, _CHUNK):
         hi = min(n, lo + _CHUNK)
         x = rng.standard_normal(hi - lo, dtype=np.float32)
+        if per_row:
+            x = x * std[np.arange(lo, hi) // inner]
+        elif std != 1.0:
+            x = x * std
         flat[lo:hi] = x.astype(np.float16) if out_dtype == "f16" else f32_to_bf16_bits(x)
     return flat.reshape(shape)
 
@@ -169,7 +180,7 @@ def build(name, seed, *, ctx, q_len, num_q_heads, num_kv_heads, head_dim,
           kv_dtype, q_dtype="f16", src_dtype="f16", pool_pages=None,
           shared_prefix_tokens=0, window_left=-1, num_sinks=0, num_splits=0,
           softmax_scale=None, ctx_range=None, batch=None, extra_stride=1,
-          kv_source=None):
+          kv_source=None, v_std=1.0):
     """Build a workload.
 
     ``ctx``: list of context lengths, or None with ``ctx_range=(lo, hi)`` and
@@ -178,6 +189,9 @@ def build(name, seed, *, ctx, q_len, num_q_heads, num_kv_heads, head_dim,
     first positions of every sequence map to the same physical pages and
     hold the same K/V.  ``kv_source``: reuse K/V/pages of another workload
     (same seed stream position), used by the sliding-window variant.
+    ``v_std``: standard deviation of the V values, a scalar or one value per
+    unique token row (small or widely varying V magnitudes probe the
+    precision of per-token scales).
     """
     rng = np.random.default_rng(seed)
     if ctx is None:
@@ -235,7 +249,7 @@ def build(name, seed, *, ctx, q_len, num_q_heads, num_kv_heads, head_dim,
                 rng.standard_normal(min(n, lo_ + _CHUNK) - lo_, dtype=np.float32)
     else:
         tokens_k = _normal(rng, shape, src_dtype)
-        tokens_v = _normal(rng, shape, src_dtype)
+        tokens_v = _normal(rng, shape, src_dtype, v_std)
     T = int(q_len.sum())
     q = _normal(rng, (T, num_q_heads, head_dim), q_dtype)
 

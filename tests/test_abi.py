@@ -47,7 +47,7 @@ def test_exports_every_declared_symbol():
 
 def test_abi_version():
     L = _lib()
-    assert L.abi_version() == 5001
+    assert L.abi_version() == 6001
 
 
 @pytest.mark.parametrize("cname,pyname", [("ra_attn_args", "AttnArgs"), ("ra_qkv_rope_args", "RopeArgs")])
@@ -78,6 +78,38 @@ def test_header_compiles_as_c_and_cpp():
             open(p, "w").write("#include \"ra_kv.h\"\nint32_t (*f)(void) = ra_abi_version;\nint main(void){return f == 0;}\n")
             subprocess.run([comp, "-Wall", "-Werror", "-Wno-address", "-c", "-I", os.path.dirname(HEADER), p, "-o",
                             os.path.join(d, "h.o")], check=True)
+
+
+def test_fused_store_targets_are_writable_fields():
+    """The fused store writes the caches and scale planes it is handed, so
+    the header declares those fields writable: a caller's mutable pointer goes
+    in, and a writable pointer comes back out, with no cast, under -Werror in
+    C and C++."""
+    code = ('#include "ra_kv.h"\n'
+            'int main(void) {\n'
+            '  ra_attn_args a = {0};\n'
+            '  static unsigned char kc[16], vc[16];\n'
+            '  static float ks[16], vs[16];\n'
+            '  a.k_cache = kc; a.v_cache = vc; a.k_scales = ks; a.v_scales = vs;\n'
+            '  unsigned char* k = (unsigned char*)0; float* s = a.k_scales; void* v = a.v_cache;\n'
+            '  k = (unsigned char*)a.k_cache;\n'
+            '  return (k != kc) + (s != ks) + (v != vc) + (a.v_scales != vs);\n'
+            '}\n')
+    with tempfile.TemporaryDirectory() as d:
+        for comp, ext in (("gcc", "c"), ("g++", "cpp")):
+            p = os.path.join(d, "w." + ext)
+            open(p, "w").write(code)
+            exe = os.path.join(d, "w_" + ext)
+            subprocess.run([comp, "-Wall", "-Werror", "-Wcast-qual", "-I", os.path.dirname(HEADER), p, "-o", exe],
+                           check=True)
+            assert subprocess.run([exe]).returncode == 0
+    text = open(HEADER).read()
+    body = text[text.index("typedef struct ra_attn_args"):text.index("} ra_attn_args;")]
+    for f in ("k_cache", "v_cache", "k_scales", "v_scales"):
+        decl = re.search(rf"^\s*([^;]*)\b{f};", body, re.M).group(1)
+        assert "const" not in decl, f"{f} is declared read-only: {decl!r}"
+    # the precondition on pages that take new tokens is stated with the fused store
+    assert "must be read by no other sequence" in text
 
 
 FAKE = 0x100000      # 16-byte aligned, never dereferenced by validation

@@ -249,3 +249,31 @@ def test_context_shorter_than_block_is_nan_not_fault():
     q0, q1 = int(w.query_start_loc[3]), int(w.query_start_loc[4])
     assert torch.isnan(out[q0:q1]).all()
     assert torch.isfinite(out[:q0]).all()
+
+
+# Per-token INT8 keeps its precision whatever the magnitude of V: the V
+# scales ride on the fp16 probabilities relative to a power-of-two reference,
+# so p * vs stays in fp16's normal range for small V, and a reference that
+# moves up as larger scales arrive rescales what was accumulated exactly.
+# The elementwise bound is dominated by its absolute term at these output
+# magnitudes; the per-row normwise bound (1e-2) is what these cases test.
+def _int8tok_vstd(kind, U):
+    if kind == "growing":      # 2^-20 .. 1 along the unique token rows: the reference moves many times
+        return np.exp2(np.linspace(-20.0, 0.0, U)).astype(np.float32)
+    if kind == "shrinking":    # 1 .. 2^-20: later tokens far below the reference
+        return np.exp2(np.linspace(0.0, -20.0, U)).astype(np.float32)
+    return float(kind)
+
+
+@pytest.mark.parametrize("kind", ["1e-2", "1e-3", "1e-4", "growing", "shrinking"])
+@pytest.mark.parametrize("ql,S", [(5, 0), (1, 3), (16, 1)], ids=["verify_auto", "decode_split3", "q16_direct"])
+def test_int8tok_precision_independent_of_v_magnitude(kind, ql, S):
+    ctx = [3000, 700, 77]
+    U = sum(ctx)
+    pool = int(sum(-(-c // 16) for c in ctx) * 1.25) + 3
+    w = W.build(f"int8tok_v{kind}", 23, ctx=ctx, q_len=ql, num_q_heads=16, num_kv_heads=2, head_dim=128,
+                kv_dtype="int8_tok", pool_pages=pool, num_splits=S, v_std=_int8tok_vstd(kind, U))
+    dw = DeviceWorkload(w)
+    out, lse = dw.attn()
+    torch.cuda.synchronize()
+    _check_all(w, out, lse, f"int8tok V {kind} q_len {ql} S {S}")

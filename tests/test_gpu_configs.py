@@ -1,13 +1,14 @@
 """GPU parity on the benchmark workloads at full size, in the launch
 configuration bench.py times.
 
-Store: bit-exact on a random sample of tokens (their bytes in the GPU caches
-against the oracle's codes at the layout's offsets) plus the untouched
-sentinel of an unused page.  Attention: every output of sampled
-(sequence, KV head) units against the fp64 oracle computed one unit at a
-time.  As in bench.py, decode and verify workloads (at most 48 rows per KV
-head) store the step's own tokens inside the attention launch; the store
-sample is drawn after it and always includes some of those tokens.
+Store: bit-exact on 4096 random tokens plus every token the step itself
+stores (their bytes in the GPU caches against the oracle's codes at the
+layout's offsets) and the untouched sentinel of an unused page.  Attention:
+every output of every (sequence, KV head) unit against the fp64 oracle,
+computed one unit at a time; the prefill workloads, whose blocks hold
+thousands of queries, compare sampled query rows of every unit.  As in
+bench.py, decode and verify workloads (at most 48 rows per KV head) store
+the step's own tokens inside the attention launch.
 """
 import numpy as np
 import pytest
@@ -20,21 +21,22 @@ from tests.gpu_util import DeviceWorkload, Timer, compare, log, oracle_seq, out_
 
 pytestmark = pytest.mark.gpu
 
-# workload factory, sampled (sequence, kv head) units
+# workload factory; "all": every (sequence, KV head) unit with all its
+# queries; "sample": every unit with sampled query rows (row-group edges, the
+# first and last queries, random ones)
 CONFIGS = [
-    ("tiny_decode", W.tiny_decode, [(0, 0)]),
-    ("batch8_decode", W.batch8_decode, [(b, h) for b in range(8) for h in range(2)]),
-    ("verify_fp8_32k", W.verify_fp8_32k, [(0, 0), (5, 1), (7, 1)]),
-    ("prefix_int8_256k", W.prefix_int8_256k, [(0, 1), (3, 0)]),
-    ("split_fp8_512k", W.split_fp8_512k, [(1, 0)]),
+    ("tiny_decode", W.tiny_decode, "all"),
+    ("batch8_decode", W.batch8_decode, "all"),
+    ("verify_fp8_32k", W.verify_fp8_32k, "all"),
+    ("prefix_int8_256k", W.prefix_int8_256k, "all"),
+    ("split_fp8_512k", W.split_fp8_512k, "all"),
     # beyond the five: plain decode at 32K, and per-token INT8 at the verify shape
-    ("decode_fp8_32k", W.decode_fp8_32k, [(2, 1)]),
-    ("verify_int8tok_32k", W.verify_int8tok_32k, [(0, 1), (6, 0)]),
-    # prefill: sampled query rows (row-group edges, the first and last queries,
-    # random ones) of each sampled KV head
-    ("prefill_fp8_8k", W.prefill_fp8_8k, [(0, 0, "sample"), (0, 1, "sample")]),
-    ("chunk_prefill_fp8_128k", W.chunk_prefill_fp8_128k, [(0, 1, "sample")]),
+    ("decode_fp8_32k", W.decode_fp8_32k, "all"),
+    ("verify_int8tok_32k", W.verify_int8tok_32k, "all"),
+    ("prefill_fp8_8k", W.prefill_fp8_8k, "sample"),
+    ("chunk_prefill_fp8_128k", W.chunk_prefill_fp8_128k, "sample"),
 ]
+STORE_SAMPLE = 4096
 
 
 def _query_sample(w, b, seed):
@@ -49,7 +51,7 @@ def _query_sample(w, b, seed):
     return np.unique(np.clip(rows, 0, ql - 1))
 
 
-def _check_store_sample(w, dw, n=48, seed=0, extra_rows=None):
+def _check_store_sample(w, dw, n=STORE_SAMPLE, seed=0, extra_rows=None):
     rng = np.random.default_rng(seed)
     rows = rng.choice(w.tokens_k.shape[0], size=min(n, w.tokens_k.shape[0]), replace=False)
     if extra_rows is not None:
@@ -81,7 +83,7 @@ def _check_store_sample(w, dw, n=48, seed=0, extra_rows=None):
             assert np.all(blk == w.cache_sentinel)
 
 
-def _run(name, make, units, base=None):
+def _run(name, make, mode, base=None):
     with Timer(f"{name}: build"):
         w = make() if base is None else make(base)
     fused = (w.num_q_heads // w.num_kv_heads) * w.max_q_len <= 48
@@ -91,18 +93,24 @@ def _run(name, make, units, base=None):
     with Timer(f"{name}: attention{' with the fused store' if fused else ''}"):
         out, lse = dw.attn()
         torch.cuda.synchronize()
-    _check_store_sample(w, dw, extra_rows=w.new_token_rows()[:8] if fused else None)
+    with Timer(f"{name}: store check ({STORE_SAMPLE} random tokens + the step's own)"):
+        _check_store_sample(w, dw, extra_rows=w.new_token_rows())
     out = out_to_np(out)
     lse = lse.cpu().numpy().astype(np.float64)
-    for unit in units:
-        b, h = unit[:2]
-        q0, q1 = int(w.query_start_loc[b]), int(w.query_start_loc[b + 1])
-        cols = qhead_cols(w, [h])
-        q_rows = _query_sample(w, b, seed=h) if len(unit) > 2 else np.arange(q1 - q0)
-        with Timer(f"{name}: oracle seq {b} kv head {h}, {q_rows.size} queries"):
-            ro, rl = oracle_seq(w, b, kv_heads=[h], q_rows=q_rows if len(unit) > 2 else None)
-        e = compare(out[q0:q1][q_rows][:, cols], lse[q0:q1][q_rows][:, cols], ro, rl, f"{name} seq {b} head {h}")
-        log(f"{name} seq {b} head {h}: max abs {e[0]:.2e} normwise {e[1]:.2e} lse {e[2]:.2e}")
+    worst = (0.0, 0.0, 0.0)
+    with Timer(f"{name}: oracle over {w.batch} x {w.num_kv_heads} units"):
+        for b in range(w.batch):
+            q0, q1 = int(w.query_start_loc[b]), int(w.query_start_loc[b + 1])
+            for h in range(w.num_kv_heads):
+                cols = qhead_cols(w, [h])
+                sample = mode == "sample"
+                q_rows = _query_sample(w, b, seed=h) if sample else np.arange(q1 - q0)
+                ro, rl = oracle_seq(w, b, kv_heads=[h], q_rows=q_rows if sample else None)
+                e = compare(out[q0:q1][q_rows][:, cols], lse[q0:q1][q_rows][:, cols], ro, rl,
+                            f"{name} seq {b} head {h}")
+                worst = tuple(max(x, y) for x, y in zip(worst, e))
+    log(f"{name}: every unit within tolerance; worst max abs {worst[0]:.2e} normwise {worst[1]:.2e} "
+        f"lse {worst[2]:.2e}")
     assert np.isfinite(out).all()
     return w
 
@@ -110,11 +118,11 @@ def _run(name, make, units, base=None):
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("cfg", CONFIGS, ids=[c[0] for c in CONFIGS])
 def test_benchmark_workload(cfg):
-    name, make, units = cfg
-    _run(name, make, units)
+    name, make, mode = cfg
+    _run(name, make, mode)
 
 
 @pytest.mark.timeout(900)
 def test_sliding_window_workload():
     base = W.split_fp8_512k()
-    _run("split_fp8_512k_sliding", W.split_fp8_512k_sliding, [(0, 1), (1, 0)], base=base)
+    _run("split_fp8_512k_sliding", W.split_fp8_512k_sliding, "all", base=base)

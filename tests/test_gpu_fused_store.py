@@ -205,3 +205,109 @@ def test_fused_rope_equals_qkv_rope_store_then_attention(case):
     assert torch.equal(_bits(oA), _bits(oB)), f"{name}: outputs differ"
     assert torch.equal(_bits(lA), _bits(lB)), f"{name}: lse differs"
     log(f"{name}: RoPE + fused store in the attention launch == ra_qkv_rope_store + ra_paged_attn, bit for bit")
+
+
+def _oracle_fused_rope_attention(w, qkv_host, src, pos, slots, table32, rot):
+    """The oracle's answer for one attention launch with the fused store and
+    RoPE: older tokens dequantised from their codes, the block's own tokens
+    rotated, quantised and dequantised by oracle.rope.qkv_rope_store (tokens
+    it does not store read back the caches' zero fill), and fp64 attention
+    with the rotated queries."""
+    from oracle import attention as OA
+    from oracle import codecs as OC
+    from oracle import layout as OL
+    from oracle import rope as R
+    from tests.gpu_util import dequant_tokens
+    hq, hkv, D, kv = w.num_q_heads, w.num_kv_heads, w.head_dim, w.kv_dtype
+    T = qkv_host.shape[0]
+    packed = (hq + 2 * hkv) * D
+    local = np.where(slots >= 0, np.arange(T, dtype=np.int64), -1)     # one scratch slot per token
+    e = 2 if kv == "f16" else 1
+    npg = -(-T // 16)
+    zc = np.zeros(npg * hkv * 16 * D * e, np.uint8)
+    zp = np.zeros(npg * hkv * 16, np.float32)
+    q_rot, kc, vc, ks, vs = R.qkv_rope_store(np.ascontiguousarray(qkv_host[:, :packed]), src, pos, table32, rot,
+                                             hq, hkv, D, local, zc, zc.copy(), kv, w.k_scale, w.v_scale,
+                                             zp, zp.copy())
+    idx = np.arange(T, dtype=np.int64)
+    kq = OL.gather(kc, idx, "k", hkv, D, kv)
+    vq = OL.gather(vc, idx, "v", hkv, D, kv)
+    if kv == "int8_tok":
+        k_new = OC.dequantize_per_token(kq, OL.gather_scales(ks, idx, hkv))
+        v_new = OC.dequantize_per_token(vq, OL.gather_scales(vs, idx, hkv))
+    else:
+        k_new = OC.dequantize(kq, kv, w.k_scale)
+        v_new = OC.dequantize(vq, kv, w.v_scale)
+    q64 = OC.source_to_f32(q_rot, src).astype(np.float64)
+    outs, lses = [], []
+    for b in range(w.batch):
+        q0, q1 = int(w.query_start_loc[b]), int(w.query_start_loc[b + 1])
+        old = w.seq_rows[b][:int(w.ctx[b]) - (q1 - q0)]
+        k = np.concatenate([dequant_tokens(w, old, "k"), k_new[q0:q1]])
+        v = np.concatenate([dequant_tokens(w, old, "v"), v_new[q0:q1]])
+        o, l = OA.attention(q64[q0:q1], k, v, w.softmax_scale)
+        outs.append(o)
+        lses.append(l)
+    return np.concatenate(outs), np.concatenate(lses)
+
+
+ROPE_ORACLE_CASES = ROPE_CASES + [
+    ("verify_e4m3_yarn_direct", [1000, 77, 513, 4097], 5, 16, 2, 128, "e4m3", "f16", 128, 2.0, 1),
+]
+
+
+@pytest.mark.parametrize("case", ROPE_ORACLE_CASES, ids=[c[0] for c in ROPE_ORACLE_CASES])
+def test_fused_rope_attention_matches_oracle(case):
+    """One attention launch with RoPE and the fused store against the oracle
+    directly.  The last token of sequence 0 has a position outside the
+    table: its Q rows are NaN, so its out and lse must come back NaN (with
+    one partition slot and with several), and nothing is stored for it; the
+    last token of sequence 1 is padding (slot -1).  The caches start zeroed,
+    so the positions of unstored tokens read back zeros on both sides."""
+    from oracle import rope as R
+    from tests.gpu_util import compare, out_to_np
+    name, ctx, ql, hq, hkv, D, kv, src, rot, factor, S = case
+    pool = int(sum(-(-c // 16) for c in ctx) * 1.25) + 3
+    w = W.build(name, 54, ctx=ctx, q_len=ql, num_q_heads=hq, num_kv_heads=hkv, head_dim=D, kv_dtype=kv,
+                q_dtype=src, src_dtype=src, pool_pages=pool, num_splits=S)
+    new_rows = w.new_token_rows()
+    old_rows = np.setdiff1d(np.arange(w.tokens_k.shape[0]), new_rows)
+    pos, slots = W.step_positions_and_slots(w)
+    pos, slots = pos.copy(), slots.copy()
+    max_pos = int(pos.max()) + 1
+    qsl = w.query_start_loc
+    pos[int(qsl[1]) - 1] = max_pos                # outside the table
+    slots[int(qsl[2]) - 1] = -1                   # padding
+    T = len(pos)
+    qkv_host = W.packed_qkv(54, T, hq, hkv, D, src, row_pad=8)
+    table32 = R.rope_table(max_pos, rot, 1e6, factor, original_max=max(1, max_pos // 2)).astype(np.float32)
+    qkv = t_src(qkv_host, src)
+    kc = P.new_cache(w.num_pages, hkv, D, kv, fill=0)
+    vc = P.new_cache(w.num_pages, hkv, D, kv, fill=0)
+    ks = vs = None
+    if kv == "int8_tok":
+        ks, vs = P.new_scale_plane(w.num_pages, hkv, fill=0.0), P.new_scale_plane(w.num_pages, hkv, fill=0.0)
+    P.kv_store(t_src(w.tokens_k[old_rows], src), t_src(w.tokens_v[old_rows], src),
+               torch.from_numpy(w.token_slots[old_rows]).cuda(), kc, vc, kv, w.k_scale, w.v_scale,
+               k_scales=ks, v_scales=vs)
+    out, lse = P.paged_attn(qkv[:, :hq * D].view(T, hq, D), kc, vc, torch.from_numpy(w.block_tables).cuda(),
+                            torch.from_numpy(w.ctx).cuda(), torch.from_numpy(qsl).cuda(),
+                            kv_dtype=kv, k_scale=w.k_scale, v_scale=w.v_scale, softmax_scale=w.softmax_scale,
+                            max_q_len=w.max_q_len, min_q_len=int(w.q_len.min()), max_context_len=w.max_context_len,
+                            num_splits=S, k_scales=ks, v_scales=vs,
+                            new_k=qkv[:, hq * D:(hq + hkv) * D].view(T, hkv, D),
+                            new_v=qkv[:, (hq + hkv) * D:(hq + 2 * hkv) * D].view(T, hkv, D),
+                            new_slots=torch.from_numpy(slots).cuda(), rope_table=torch.from_numpy(table32).cuda(),
+                            positions=torch.from_numpy(pos).cuda(), rotary_dim=rot)
+    torch.cuda.synchronize()
+    ro, rl = _oracle_fused_rope_attention(w, qkv_host, src, pos, slots, table32, rot)
+    got_o = out_to_np(out)
+    got_l = lse.cpu().numpy().astype(np.float64)
+    nan_tok = int(qsl[1]) - 1
+    assert np.isnan(ro[nan_tok]).all() and np.isnan(rl[nan_tok]).all()
+    assert np.isnan(got_o[nan_tok]).all(), f"{name}: out of the out-of-table token is not NaN"
+    assert np.isnan(got_l[nan_tok]).all(), f"{name}: lse of the out-of-table token is not NaN"
+    keep = np.ones(T, bool)
+    keep[nan_tok] = False
+    e = compare(got_o[keep], got_l[keep], ro[keep], rl[keep], name)
+    log(f"{name}: fused RoPE attention vs oracle: max abs {e[0]:.2e} normwise {e[1]:.2e} lse {e[2]:.2e}")
