@@ -285,7 +285,7 @@ __device__ __forceinline__ void take_v_scales(Acc<KV, D, NT>& acc, const f32x4& 
   float vm = fmaxf(fmaxf(vs[0], vs[1]), fmaxf(vs[2], vs[3]));
   vm = fmaxf(vm, __shfl_xor(vm, 16));   // the lanes' token quads: kgrp = lane bits 4, 5
   vm = fmaxf(vm, __shfl_xor(vm, 32));
-  vm = __builtin_amdgcn_readfirstlane(vm);
+  vm = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(vm)));   // (the builtin takes an int)
   if (vm > acc.vref * 128.0f) {
     int32_t e = (int32_t)((__float_as_uint(vm) >> 23) & 0xFFu) - 126;   // vm = f * 2^e, f in [0.5, 1)
     e = min(max(e, -119), 120);                                         // vref and 1 / vref stay normal

@@ -256,7 +256,9 @@ def test_context_shorter_than_block_is_nan_not_fault():
 # so p * vs stays in fp16's normal range for small V, and a reference that
 # moves up as larger scales arrive rescales what was accumulated exactly.
 # The elementwise bound is dominated by its absolute term at these output
-# magnitudes; the per-row normwise bound (1e-2) is what these cases test.
+# magnitudes; the per-row normwise bound (1e-2) is what these cases test.  The
+# queries, and so the outputs, are bf16: outputs near 1e-7 are subnormal in
+# fp16 and would carry the output format's rounding, not the kernel's.
 def _int8tok_vstd(kind, U):
     if kind == "growing":      # 2^-20 .. 1 along the unique token rows: the reference moves many times
         return np.exp2(np.linspace(-20.0, 0.0, U)).astype(np.float32)
@@ -272,7 +274,8 @@ def test_int8tok_precision_independent_of_v_magnitude(kind, ql, S):
     U = sum(ctx)
     pool = int(sum(-(-c // 16) for c in ctx) * 1.25) + 3
     w = W.build(f"int8tok_v{kind}", 23, ctx=ctx, q_len=ql, num_q_heads=16, num_kv_heads=2, head_dim=128,
-                kv_dtype="int8_tok", pool_pages=pool, num_splits=S, v_std=_int8tok_vstd(kind, U))
+                kv_dtype="int8_tok", q_dtype="bf16", pool_pages=pool, num_splits=S,
+                v_std=_int8tok_vstd(kind, U))
     dw = DeviceWorkload(w)
     out, lse = dw.attn()
     torch.cuda.synchronize()
