@@ -88,7 +88,7 @@
 extern "C" {
 #endif
 
-#define RA_KV_ABI_VERSION 6
+#define RA_KV_ABI_VERSION 7
 #define RA_KV_LAYOUT_ID 1
 #define RA_KV_PAGE_SIZE 16
 #define RA_KV_MAX_SPLITS 4096
@@ -375,6 +375,25 @@ int32_t ra_paged_attn(const ra_attn_args* args, void* stream);
 int32_t ra_paged_attn_workspace(const ra_attn_args* args, int32_t* slots,
                                 int64_t* partial_out_floats,
                                 int64_t* partial_lse_floats);
+
+/*
+ * ra_paged_attn_noalloc -- ra_paged_attn for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same attention, kernels and results, but the
+ * partials of a split call live in a scratch array of the library's own,
+ * RA_KV_NOALLOC_SCRATCH_BYTES bytes per GPU, held from the library's first
+ * use on that GPU until the process ends; partial_out, partial_lse and
+ * partial_slots are ignored.  out must be non-NULL (RA_ERR_INVALID_ARG).  A
+ * call whose partials, slots * total_q * num_q_heads * (head_dim + 1) * 4
+ * bytes, exceed the scratch returns RA_ERR_WORKSPACE before anything is
+ * enqueued.  The call allocates and frees nothing.  Every call on one GPU
+ * shares that GPU's scratch: calls that overlap on one GPU (on different
+ * streams, or from several threads without ordering) race and must not be
+ * issued; calls ordered on one stream are safe.  Uses the device that is
+ * current on the calling thread (it must be the stream's device).
+ */
+#define RA_KV_NOALLOC_SCRATCH_BYTES (32u << 20)
+int32_t ra_paged_attn_noalloc(const ra_attn_args* args, void* stream);
 
 /*
  * ra_lse_merge -- merge partial attention results by log-sum-exp.

@@ -117,6 +117,7 @@ EXPORTED = {
     "ra_kv_store_int8_token": (_c.c_int32, [_vp, _vp, _c.c_int32, _c.c_int64, _c.c_int64, _vp, _c.c_int64, _vp,
                                             _vp, _vp, _vp, _c.c_int64, _c.c_int32, _c.c_int32, _c.c_int32, _vp]),
     "ra_paged_attn": (_c.c_int32, [_c.POINTER(AttnArgs), _vp]),
+    "ra_paged_attn_noalloc": (_c.c_int32, [_c.POINTER(AttnArgs), _vp]),
     "ra_paged_attn_workspace": (_c.c_int32, [_c.POINTER(AttnArgs), _c.POINTER(_c.c_int32),
                                              _c.POINTER(_c.c_int64), _c.POINTER(_c.c_int64)]),
     "ra_lse_merge": (_c.c_int32, [_vp, _vp, _c.c_int32, _c.c_int64, _c.c_int32, _vp, _c.c_int32, _vp, _vp]),
@@ -289,7 +290,8 @@ def paged_attn(q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
                max_q_len, max_context_len, k_scale=1.0, v_scale=1.0, softmax_scale=None, min_q_len=0,
                window_left=-1, num_sinks=0, num_splits=0, out=None, lse=None, partials_only=False,
                workspace=None, stream=None, k_scales=None, v_scales=None, kv_pos0=None, q_pos0=None,
-               new_k=None, new_v=None, new_slots=None, rope_table=None, positions=None, rotary_dim=None):
+               new_k=None, new_v=None, new_slots=None, rope_table=None, positions=None, rotary_dim=None,
+               no_alloc=False):
     """Attention of the query blocks over the paged caches.
 
     q [total_q][Hq][D] fp16/bf16; block_tables int32 [B][stride];
@@ -301,6 +303,9 @@ def paged_attn(q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
     rope_table [P][2][R/2] fp32 and positions int64 [total_q] (with new_k):
     q and new_k are rotated by RoPE inside the launch.  q may be a view into
     packed QKV rows (its token stride is passed on).
+    no_alloc=True calls ra_paged_attn_noalloc: the partials of a split call
+    stay in the library's static scratch and no workspace is allocated (out
+    and lse are still allocated here unless passed in).
     """
     T, hq, D = q.shape
     hkv = k_cache.shape[1]
@@ -315,6 +320,11 @@ def paged_attn(q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
             lse = torch.empty((T, hq), dtype=torch.float32, device=q.device)
         a.out = out.data_ptr()
         a.lse = lse.data_ptr()
+    if no_alloc:
+        if partials_only:
+            raise ValueError("no_alloc keeps the partials in the library's scratch: partials_only is not available")
+        _check(load_library().ra_paged_attn_noalloc(_c.byref(a), _stream(stream)))
+        return out, lse
     slots, po_n, pl_n = paged_attn_workspace(a)
     po = pl = None
     if po_n > 0 or partials_only:

@@ -10,6 +10,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -254,6 +255,39 @@ ra::AttnLaunch make_launch(const ra_attn_args* a, const Plan& p) {
   return L;
 }
 
+// ---------------------------------------------------------------------------
+// Scratch of the no-allocation entry point: the fp32 partials of the split
+// KV partitions live in this array instead of a caller's workspace.  Each GPU
+// the library runs on holds its own copy for the life of the process.  Host
+// code never passes the array's name to a kernel (on the host it is only a
+// stand-in for the symbol); it passes the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device on first use.
+constexpr size_t kScratchBytes = (size_t)RA_KV_NOALLOC_SCRATCH_BYTES;
+static __device__ __attribute__((aligned(256))) float scratch[kScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int32_t scratch_address(const char* fn, float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(RA_ERR_HIP, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(RA_ERR_UNSUPPORTED, "%s: device index %d >= %d", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(RA_ERR_HIP, "%s: hipGetSymbolAddress of the scratch array failed on device %d: %s", fn, dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<float*>(g_scratch_ptr[dev]);
+  return RA_OK;
+}
+
 int32_t store_common(const char* fn, const void* k, const void* v, int32_t src_dtype, int64_t k_token_stride,
                      int64_t v_token_stride, const int64_t* slot_mapping, int64_t num_tokens, void* k_cache,
                      void* v_cache, int32_t kv_dtype, float* k_scales, float* v_scales, int64_t num_pages,
@@ -371,6 +405,36 @@ int32_t ra_paged_attn(const ra_attn_args* args, void* stream) {
     if (e != hipSuccess) return fail(RA_ERR_HIP, "ra_paged_attn: merge launch failed: %s", hipGetErrorString(e));
   }
   return RA_OK;
+}
+
+int32_t ra_paged_attn_noalloc(const ra_attn_args* args, void* stream) {
+  static const char* fn = "ra_paged_attn_noalloc";
+  Plan p{};
+  int32_t st = check_attn(args, &p);
+  if (st != RA_OK) return st;
+  if (args->batch == 0 || args->total_q == 0) return RA_OK;
+  if (!args->out)
+    return fail(RA_ERR_INVALID_ARG, "%s: out must be non-NULL (the partials stay in the library's scratch)", fn);
+  ra_attn_args a = *args;
+  if (!p.direct) {
+    // partial_out [slots][rows][D] then partial_lse [slots][rows]; rows * D is
+    // a multiple of 64 floats, so the lse part stays 16-byte aligned
+    const int64_t rows = (int64_t)args->total_q * args->num_q_heads;
+    const int64_t out_floats = (int64_t)p.slots * rows * args->head_dim;
+    const int64_t bytes = (out_floats + (int64_t)p.slots * rows) * (int64_t)sizeof(float);
+    if (bytes > (int64_t)kScratchBytes)
+      return fail(RA_ERR_WORKSPACE,
+                  "%s: %d partition slot(s) x %lld rows need %lld bytes of partials, more than the %zu-byte "
+                  "static scratch; call ra_paged_attn with a workspace", fn, p.slots, (long long)rows,
+                  (long long)bytes, kScratchBytes);
+    float* base = nullptr;
+    st = scratch_address(fn, &base);
+    if (st != RA_OK) return st;
+    a.partial_out = base;
+    a.partial_lse = base + out_floats;
+    a.partial_slots = p.slots;
+  }
+  return ra_paged_attn(&a, stream);
 }
 
 int32_t ra_lse_merge(const float* partial_out, const float* partial_lse, int32_t num_partitions, int64_t rows,

@@ -47,7 +47,7 @@ def test_exports_every_declared_symbol():
 
 def test_abi_version():
     L = _lib()
-    assert L.abi_version() == 6001
+    assert L.abi_version() == 7001
 
 
 @pytest.mark.parametrize("cname,pyname", [("ra_attn_args", "AttnArgs"), ("ra_qkv_rope_args", "RopeArgs")])
@@ -148,6 +148,32 @@ def _good_args(L, **kw):
     for k, v in kw.items():
         setattr(a, k, v)
     return a
+
+
+def test_noalloc_validation():
+    """ra_paged_attn_noalloc: host checks before anything is enqueued.  Partials
+    beyond the static scratch (RA_KV_NOALLOC_SCRATCH_BYTES, 32 MiB) are refused
+    with RA_ERR_WORKSPACE, also one row past the limit; out must be given; an
+    empty batch is a no-op; the ordinary argument checks apply as well."""
+    L = _lib()
+    lib = L.load_library()
+    header = open(HEADER).read()
+    assert re.search(r"#define RA_KV_NOALLOC_SCRATCH_BYTES \(32u << 20\)", header)
+    limit = 32 << 20
+    # 64 slots x total_q x 16 heads x (128 + 1) x 4 bytes: 63 query tokens fit, 64 do not
+    assert 64 * 63 * 16 * 129 * 4 <= limit < 64 * 64 * 16 * 129 * 4
+    a = _good_args(L, num_splits=64, total_q=64, max_q_len=64, min_q_len=1, batch=1)
+    assert lib.ra_paged_attn_noalloc(ctypes.byref(a), None) == 4
+    assert b"static scratch" in lib.ra_last_error()
+    a = _good_args(L, num_splits=4096, total_q=1000, max_q_len=1000, min_q_len=1, batch=1)
+    assert lib.ra_paged_attn_noalloc(ctypes.byref(a), None) == 4
+    a = _good_args(L, num_splits=8, out=None)
+    assert lib.ra_paged_attn_noalloc(ctypes.byref(a), None) == 1
+    assert b"out must be non-NULL" in lib.ra_last_error()
+    a = _good_args(L, batch=0, total_q=0, q=None, out=None)
+    assert lib.ra_paged_attn_noalloc(ctypes.byref(a), None) == 0
+    for kw, status in ((dict(head_dim=96), 2), (dict(k_scale=0.0), 1), (dict(struct_size=8), 1)):
+        assert lib.ra_paged_attn_noalloc(ctypes.byref(_good_args(L, **kw)), None) == status, kw
 
 
 BAD_ATTN = [
