@@ -75,6 +75,13 @@ def parse():
                     help="launch every step from the host instead of replaying captured HIP graphs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (for counter scaling)")
+    ap.add_argument("--timeline", action="store_true",
+                    help="per-workgroup phase timings of the attention kernel, from the timing build "
+                         "libra_kv_timeline.so (python -m paged_quantized_kv_ra_amd.build --timeline)")
+    ap.add_argument("--timeline-launches", type=int, default=20)
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="HBM read rate of random 2/4/8 KiB blocks read the way the attention reads pages "
+                         "(libra_probe.so), against a streaming read")
     return ap.parse_args()
 
 
@@ -411,8 +418,145 @@ def time_eager(step, args, torch):
     return start.elapsed_time(stop) / args.steps, sum(attn_ms) / len(attn_ms), wall
 
 
+def read_ceiling(torch):
+    """Read rates of a 2 GiB buffer by libra_probe.so (block reads at a random
+    permutation of block ids, 8-wave workgroups, two blocks in flight per
+    wave; see probe/read_ceiling.hip), best and median of 5 timed launches
+    after one untimed."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "paged_quantized_kv_ra_amd", "libra_probe.so"))
+    fn = lib.ra_probe_read_blocks
+    fn.restype = ctypes.c_int32
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                   ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    n = 2 << 30
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    out = torch.empty(1024 * 512, dtype=torch.int32, device="cuda")
+    gen = torch.Generator().manual_seed(1)
+    perms = {bb: torch.randperm(n // bb, generator=gen).to(torch.int32).cuda() for bb in (2048, 4096, 8192)}
+    modes = {0: "LDS DMA ring, default policy", 1: "LDS DMA ring, nontemporal", 2: "plain loads, default policy",
+             3: "plain loads, nontemporal", 4: "plain loads, nontemporal, in buffer order (streaming)"}
+    # (mode, block bytes, workgroups, workgroups per CU): extra LDS pins the count per CU
+    cases = [(4, 2048, 256, 1), (2, 2048, 256, 1), (3, 2048, 256, 1), (0, 2048, 256, 1), (1, 2048, 256, 1),
+             (2, 4096, 256, 1), (3, 4096, 256, 1), (2, 8192, 256, 1), (3, 8192, 256, 1),
+             (1, 2048, 512, 2), (3, 2048, 512, 2), (1, 2048, 1024, 4)]
+    sp = torch.cuda.current_stream().cuda_stream
+    results = []
+    for mode, bb, grid, per_cu in cases:
+        static = {0: 16 * bb, 1: 16 * bb}.get(mode, 0)
+        dyn = max(0, (160 * 1024) // per_cu - static - 1024) if per_cu == 1 else \
+            max(0, (160 * 1024) // (per_cu + 1) + 1024 - static)
+        dyn = min(dyn, 96 * 1024)
+        ts = []
+        for r in range(6):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            st = fn(buf.data_ptr(), perms[bb].data_ptr(), n // bb, bb, mode, grid, dyn, out.data_ptr(), sp)
+            b.record()
+            if st != 0:
+                raise RuntimeError(f"ra_probe_read_blocks refused mode {mode} block {bb} grid {grid}")
+            torch.cuda.synchronize()
+            if r:
+                ts.append(a.elapsed_time(b))
+        ts.sort()
+        best, med = n / (ts[0] * 1e-3) / 1e9, n / (ts[len(ts) // 2] * 1e-3) / 1e9
+        results.append({"mode": modes[mode], "block_bytes": bb, "workgroups": grid, "per_cu": per_cu,
+                        "best_gbs": round(best, 1), "median_gbs": round(med, 1)})
+        log(f"{modes[mode]:55s} {bb:5d} B blocks, {grid:4d} workgroups ({per_cu}/CU): best {best:7.1f} GB/s, "
+            f"median {med:7.1f} GB/s")
+    print(json.dumps({"read_ceiling": results}), flush=True)
+
+
+def _pct(x):
+    import numpy as np
+    x = np.asarray(x, dtype=np.float64)
+    if x.size == 0:
+        return None
+    return {"p10": round(float(np.percentile(x, 10)), 2), "median": round(float(np.median(x)), 2),
+            "p90": round(float(np.percentile(x, 90)), 2), "max": round(float(x.max()), 2)}
+
+
+def timeline(step, args, torch):
+    """Per-workgroup phases of the attention kernel from the timing build.
+    Every launch is the step's attention launch alone (with its fused store),
+    after warm-up steps; the kernel records the 100 MHz real-time counter at
+    fixed points (see the RA_TIMELINE slots in attn_mfma.hip).  Times in us,
+    over all workgroups of all launches; spans per launch."""
+    import numpy as np
+    lib = step.lib
+    for name in ("ra_timeline_read", "ra_timeline_clear", "ra_timeline_layout"):
+        if not hasattr(lib, name):
+            raise RuntimeError("--timeline needs the timing build: python -m paged_quantized_kv_ra_amd.build --timeline")
+    lib.ra_timeline_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    nb, ns = ctypes.c_int32(), ctypes.c_int32()
+    lib.ra_timeline_layout(ctypes.byref(nb), ctypes.byref(ns))
+    nb, ns = nb.value, ns.value
+    TL = dict(entry=0, hwid=1, xcc=2, meta=3, idsq=4, first=5, pages=6, loop=8, comb=16, ml=17, p0w=18, p1w=19,
+              p0r=20, p1r=21, end=24)
+    sp = torch.cuda.current_stream().cuda_stream
+    for i in range(args.warmup):
+        step.run(i, sp)
+    torch.cuda.synchronize()
+    buf = np.zeros(nb * ns, dtype=np.uint64)
+    acc = {k: [] for k in ("start", "meta", "idsq", "first", "stream_wave_median", "wave_skew", "combine",
+                           "comb_barrier1", "comb_row_stats", "comb_pass0_write", "comb_pass0_reduce",
+                           "comb_pass1_write", "comb_pass1_reduce", "comb_tail", "block", "end_after_median")}
+    spans, blocks_per_cu = [], []
+    for i in range(args.timeline_launches):
+        if lib.ra_timeline_clear() != 0:
+            raise RuntimeError("ra_timeline_clear failed")
+        step.run_attention(i, sp)
+        torch.cuda.synchronize()
+        if lib.ra_timeline_read(buf.ctypes.data, buf.nbytes) != 0:
+            raise RuntimeError("ra_timeline_read failed")
+        t = buf.reshape(nb, ns).astype(np.int64)
+        live = (t[:, TL["entry"]] > 0) & (t[:, TL["end"]:TL["end"] + 8].max(axis=1) > 0) & (t[:, TL["first"]] > 0)
+        t = t[live]
+        if t.shape[0] == 0:
+            continue
+        us = 1e-2                                     # 100 MHz ticks
+        entry = t[:, TL["entry"]]
+        t0 = entry.min()
+        loops = t[:, TL["loop"]:TL["loop"] + 8]
+        ends = t[:, TL["end"]:TL["end"] + 8]
+        end = ends.max(axis=1)
+        acc["start"] += list((entry - t0) * us)
+        acc["meta"] += list((t[:, TL["meta"]] - entry) * us)
+        acc["idsq"] += list((t[:, TL["idsq"]] - entry) * us)
+        acc["first"] += list((t[:, TL["first"]] - entry) * us)
+        acc["stream_wave_median"] += list((np.median(loops, axis=1) - t[:, TL["first"]]) * us)
+        acc["wave_skew"] += list((loops.max(axis=1) - loops.min(axis=1)) * us)
+        acc["combine"] += list((end - loops.max(axis=1)) * us)
+        steps = [("comb_barrier1", loops.max(axis=1), t[:, TL["comb"]]), ("comb_row_stats", t[:, TL["comb"]], t[:, TL["ml"]]),
+                 ("comb_pass0_write", t[:, TL["ml"]], t[:, TL["p0w"]]), ("comb_pass0_reduce", t[:, TL["p0w"]], t[:, TL["p0r"]]),
+                 ("comb_pass1_write", t[:, TL["p0r"]], t[:, TL["p1w"]]), ("comb_pass1_reduce", t[:, TL["p1w"]], t[:, TL["p1r"]]),
+                 ("comb_tail", t[:, TL["p1r"]], end)]
+        for k, a0, a1 in steps:
+            ok = (a0 > 0) & (a1 > 0)
+            acc[k] += list((a1[ok] - a0[ok]) * us)
+        acc["block"] += list((end - entry) * us)
+        acc["end_after_median"] += list((end - np.median(end)) * us)
+        spans.append((end.max() - t0) * us)
+        hw = t[:, TL["hwid"]]
+        cu = (t[:, TL["xcc"]] & 0xF) * 4096 + ((hw >> 13) & 0x7) * 512 + ((hw >> 12) & 1) * 256 + ((hw >> 8) & 0xF)
+        _, counts = np.unique(cu, return_counts=True)
+        blocks_per_cu.append((len(counts), float(counts.mean()), int(counts.max())))
+    res = {"workload": step.w.name, "launches": len(spans), "kernel_span_us": _pct(spans),
+           "cus_used": blocks_per_cu[-1][0] if blocks_per_cu else None,
+           "blocks_per_cu_max": max(b[2] for b in blocks_per_cu) if blocks_per_cu else None,
+           "phases_us": {k: _pct(v) for k, v in acc.items()}}
+    log(f"timeline of {step.w.name}: {len(spans)} launches, kernel span (first workgroup start to last end) "
+        f"{res['kernel_span_us']}")
+    log(f"  workgroups on {res['cus_used']} distinct CUs, at most {res['blocks_per_cu_max']} per CU")
+    for k, v in res["phases_us"].items():
+        log(f"  {k:20s} {v}")
+    print(json.dumps({"timeline": res}), flush=True)
+
+
 def main():
     args = parse()
+    if args.timeline:   # the timing build of the library (same ABI)
+        os.environ["RA_KV_LIB"] = os.path.join(ROOT, "paged_quantized_kv_ra_amd", "libra_kv_timeline.so")
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this path is single-GPU "
               "by design and has no multi-GPU mode.", file=sys.stderr)
@@ -422,6 +566,9 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
+    if args.read_ceiling:
+        read_ceiling(torch)
+        return
     from paged_quantized_kv_ra_amd import workloads as W
     make = W.BENCH_WORKLOADS[args.workload]
     t0 = time.time()
@@ -429,6 +576,9 @@ def main():
     log(f"built {w.name} in {time.time() - t0:.1f}s")
     step = Step(w, fused_qkv=args.fused_qkv, separate_store=args.separate_store)
     log(f"pool copies: {step.copies}, partition slots: {step.slots}")
+    if args.timeline:
+        timeline(step, args, torch)
+        return
     if args.eager:
         ms_per_step, attn_avg_ms, wall = time_eager(step, args, torch)
     else:

@@ -8,7 +8,10 @@ torch, so the dynamic loader reuses torch's runtime and device pointers,
 streams and events are shared with torch instead of living in a second
 runtime instance.
 
-Usage: ``python -m paged_quantized_kv_ra_amd.build [--jobs N]``.
+Usage: ``python -m paged_quantized_kv_ra_amd.build [--jobs N] [--timeline]``.
+``--timeline`` builds the timing variant ``libra_kv_timeline.so`` instead
+(-DRA_TIMELINE: the attention kernel records per-workgroup timestamps that
+``bench.py --timeline`` reads); the product library is left as it is.
 """
 import argparse
 import concurrent.futures as cf
@@ -24,6 +27,10 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libra_kv.so")
+PROBE_SRC = os.path.join(HERE, "probe", "read_ceiling.hip")
+PROBE_LIB = os.path.join(HERE, "libra_probe.so")
+TIMELINE_LIB = os.path.join(HERE, "libra_kv_timeline.so")
+TIMELINE_OBJDIR = os.path.join(ROOT, "_build", "timeline")
 
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
@@ -69,8 +76,30 @@ def _compile(src, extra, objdir=OBJDIR):
     return obj, r.stderr
 
 
+def _link(objs, out):
+    tl = torch_lib_dir()
+    tmp = out + ".tmp"
+    cmd = [CLANGXX, "-shared", "-fPIC", "-o", tmp] + objs + [
+        f"-L{tl}", "-l:libamdhip64.so", f"-Wl,-rpath,{tl}", "-Wl,--no-undefined",
+        "-Wl,-z,defs"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    shutil.move(tmp, out)
+    return out
+
+
+def build_probe(objdir=OBJDIR):
+    """The HBM read-rate probe (libra_probe.so, a measurement aid that
+    bench.py --read-ceiling loads; not part of libra_kv.so)."""
+    os.makedirs(objdir, exist_ok=True)
+    obj, _ = _compile(PROBE_SRC, [], objdir)
+    return _link([obj], PROBE_LIB)
+
+
 def build(jobs=None, verbose=False, extra=None, out=LIB, objdir=OBJDIR):
-    """Compile every csrc/*.hip for gfx950 and link libra_kv.so.  Always rebuilds.
+    """Compile every csrc/*.hip for gfx950 and link libra_kv.so, then the
+    read-rate probe libra_probe.so.  Always rebuilds.
 
     ``extra``: additional hipcc flags; ``out`` / ``objdir``: where the library
     and the objects go (the in-tree paths by default).
@@ -92,15 +121,9 @@ def build(jobs=None, verbose=False, extra=None, out=LIB, objdir=OBJDIR):
                              and "target-feature" not in l and l.strip())
             if warn:
                 print(f"[{os.path.basename(s)}]\n{warn}", file=sys.stderr)
-    tl = torch_lib_dir()
-    tmp = out + ".tmp"
-    cmd = [CLANGXX, "-shared", "-fPIC", "-o", tmp] + objs + [
-        f"-L{tl}", "-l:libamdhip64.so", f"-Wl,-rpath,{tl}", "-Wl,--no-undefined",
-        "-Wl,-z,defs"]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    shutil.move(tmp, out)
+    _link(objs, out)
+    if out == LIB:
+        build_probe(objdir)
     return out
 
 
@@ -108,8 +131,13 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=None)
     ap.add_argument("-v", "--verbose", action="store_true")
+    ap.add_argument("--timeline", action="store_true",
+                    help="build the timing variant libra_kv_timeline.so (per-workgroup timestamps)")
     a = ap.parse_args()
-    print(build(a.jobs, a.verbose))
+    if a.timeline:
+        print(build(a.jobs, a.verbose, extra=["-DRA_TIMELINE=1"], out=TIMELINE_LIB, objdir=TIMELINE_OBJDIR))
+    else:
+        print(build(a.jobs, a.verbose))
 
 
 if __name__ == "__main__":

@@ -27,6 +27,41 @@
 // order at the end.
 #include "attn_common.h"
 
+#ifdef RA_TIMELINE
+// Timing build (compiled only with -DRA_TIMELINE): every workgroup records,
+// from lane 0 of the marking wave, the 100 MHz real-time counter at fixed
+// points of its life into slots of ra_timeline[block][kTlSlots], for the
+// per-phase breakdown bench.py --timeline prints.  The product build has none
+// of it.
+#ifndef RA_TIMELINE_BLOCKS
+#define RA_TIMELINE_BLOCKS 8192
+#endif
+constexpr int kTlSlots = 40;
+__device__ uint64_t ra_timeline[RA_TIMELINE_BLOCKS * kTlSlots];
+enum TlSlot {
+  TL_ENTRY = 0, TL_HWID = 1, TL_XCC = 2, TL_META = 3, TL_IDSQ = 4, TL_FIRST = 5, TL_PAGES = 6, TL_UNIT = 7,
+  TL_LOOP = 8,     // + wave: the wave left its page loop
+  TL_COMB = 16,    // every wave's (m, l) published (first combine barrier passed), wave 0
+  TL_ML = 17,      // wave 0 has the common row maxima and sums
+  TL_P0W = 18,     // + pass (0, 1): the pass's LDS writes and barrier done, wave 0
+  TL_P0R = 20,     // + pass: wave 0's sums and stores of the pass issued
+  TL_END = 24,     // + wave: the wave's last store issued
+};
+#define TL_MARK(slot)                                                                      \
+  do {                                                                                     \
+    if ((threadIdx.x & 63) == 0 && blockIdx.x < RA_TIMELINE_BLOCKS)                        \
+      ra_timeline[blockIdx.x * kTlSlots + (slot)] = __builtin_amdgcn_s_memrealtime();      \
+  } while (0)
+#define TL_VALUE(slot, v)                                                                  \
+  do {                                                                                     \
+    if ((threadIdx.x & 63) == 0 && blockIdx.x < RA_TIMELINE_BLOCKS)                        \
+      ra_timeline[blockIdx.x * kTlSlots + (slot)] = (uint64_t)(v);                         \
+  } while (0)
+#else
+#define TL_MARK(slot) do {} while (0)
+#define TL_VALUE(slot, v) do {} while (0)
+#endif
+
 namespace ra {
 namespace {
 
@@ -542,6 +577,7 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
   // one field of each 64-byte line of the launch arguments, so that the
   // scalar loads of all of them are in flight together before the first branch
   asm volatile("" ::"s"(a.q), "s"(a.batch), "s"(a.slots), "s"(a.kv_pos0), "s"(a.positions));
+  if (threadIdx.x < 64) TL_MARK(TL_ENTRY);
   UnitId u;
   if (!decode_unit(a, row_groups, u)) return;
   const int lane = threadIdx.x & 63;
@@ -557,6 +593,14 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
   const int32_t qp0 = a.q_pos0 ? a.q_pos0[u.b] : 0;
   asm volatile("" ::"v"(q0), "v"(q1), "v"(ctx), "v"(kv0), "v"(qp0));
   if (q0 < 0 || q1 < q0 || q1 > a.total_q) return;      // rows not addressable
+#ifdef RA_TIMELINE
+  if (threadIdx.x < 64) {
+    TL_MARK(TL_META);
+    TL_VALUE(TL_HWID, __builtin_amdgcn_s_getreg((31 << 11) | 4));    // HW_ID
+    TL_VALUE(TL_XCC, __builtin_amdgcn_s_getreg((31 << 11) | 20));    // XCC_ID
+    TL_VALUE(TL_UNIT, ((uint64_t)u.b << 32) | ((uint64_t)u.h << 24) | ((uint64_t)u.rg << 16) | (uint64_t)u.s);
+  }
+#endif
   const int32_t g = a.hq / a.hkv;
   const int32_t q_len = q1 - q0;
   const int32_t rows = g * q_len;
@@ -621,6 +665,10 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
   if (a.new_k != nullptr && !bad) stored = store_new_tokens<KV, D>(a, u.h, q0, q_len, fr.pmin, lo, hi);
   wait_vmcnt<0>();   // the first id chunks and the query rows have landed, and the stores have completed
   if (stored) __syncthreads();   // before any wave's page loads can read a stored token
+  if (wave == 0) {
+    TL_MARK(TL_IDSQ);
+    TL_VALUE(TL_PAGES, npages);
+  }
   f16x8 qf[NT][G::KS];
   if (a.rope == nullptr) {
 #pragma unroll
@@ -730,6 +778,9 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
             wait_vmcnt<(NR - 1) * G::OPS>();
           else
             wait_vmcnt<0>();
+#ifdef RA_TIMELINE
+          if (k == 0 && wave == 0) TL_MARK(TL_FIRST);
+#endif
           PageRegs<KV, D> r;
           read_page<KV, D>(r, ring + j * G::NSL, scl + j * 32, lane_off, kgrp);
           float p[NT][4];
@@ -756,6 +807,7 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
     if (my_pages & 1) pv_single<KV, D, NT>(acc, pend_v, pend_p);
   }
   wait_vmcnt<0>();   // no ring load may land after the ring becomes the merge buffer
+  TL_MARK(TL_LOOP + wave);
 
   // ---- combine the waves.  Every wave publishes its rows' (m, l) and its
   // bad flag, then rescales its O to the common row maximum.
@@ -776,6 +828,7 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
   }
   if (lane == 0) sm_bad[wave] = bad ? 1 : 0;
   __syncthreads();
+  if (wave == 0) TL_MARK(TL_COMB);
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) bad = bad || sm_bad[w] != 0;
   float Mrow[NT], Lrow[NT], fself[NT];
@@ -807,6 +860,7 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
     Lrow[nt] = L;
     if constexpr (KV == KV_I8T) fself[nt] *= acc.vref;   // O back from units of the wave's reference
   }
+  if (wave == 0) TL_MARK(TL_ML);
 
   // ---- reduce-scatter of O through LDS, in two passes over the lane's
   // accumulator components i (pass p: i = 2p, 2p + 1).  The lane's values
@@ -829,6 +883,7 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
             fself[nt];
     }
     __syncthreads();
+    if (wave == 0) TL_MARK(TL_P0W + p);
     if (wave < kPairs) {
       const int pr = wave;
       const int nt = pr >> 1, i = 2 * p + (pr & 1);
@@ -895,8 +950,10 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
         }
       }
     }
+    if (wave == 0) TL_MARK(TL_P0R + p);
     if (p == 0) __syncthreads();   // the second pass reuses the buffer
   }
+  TL_MARK(TL_END + wave);
 }
 
 template <int KV, int D, int NT>
@@ -943,3 +1000,22 @@ hipError_t launch_attn_mfma(const AttnLaunch& a, hipStream_t s) {
 }
 
 }  // namespace ra
+
+#ifdef RA_TIMELINE
+// Timing build only: copy the timeline to host memory, or clear it.
+extern "C" int32_t ra_timeline_read(void* host, size_t bytes) {
+  if (bytes > sizeof(ra_timeline)) bytes = sizeof(ra_timeline);
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(ra_timeline), bytes, 0, hipMemcpyDeviceToHost) == hipSuccess ? 0 : 5;
+}
+extern "C" int32_t ra_timeline_clear(void) {
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(ra_timeline)) != hipSuccess) return 5;
+  if (hipMemset(p, 0, sizeof(ra_timeline)) != hipSuccess) return 5;
+  return hipDeviceSynchronize() == hipSuccess ? 0 : 5;
+}
+extern "C" int32_t ra_timeline_layout(int32_t* blocks, int32_t* slots) {
+  *blocks = RA_TIMELINE_BLOCKS;
+  *slots = kTlSlots;
+  return 0;
+}
+#endif
