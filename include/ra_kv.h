@@ -260,7 +260,14 @@ int32_t ra_qkv_rope_store(const ra_qkv_rope_args* args, void* stream);
  *   rows_b >= 16: P_b = max(2048, 16 * ceil(ceil(ctx_b / n_b) / 16)) with
  *     n_b = ceil(2048 / u_b) partitions wanted, u_b = Hkv * ceil(rows_b / 48)
  *     workgroups per partition (n_b = 1 once u_b >= 2048: a long prefill
- *     chunk is attended in one pass).
+ *     chunk is attended in one pass);
+ *   with a window (window_left >= 0), whatever the rows: only the sinks and
+ *     the window span hold visible keys, so the partitions cut that span
+ *     instead of [0, ctx_b): with base = 16 * floor(max(0, pos_first -
+ *     window_left + 1) / 16) (pos_first the block's first query), partition
+ *     s covers [base + s * P, base + (s + 1) * P), partition 0 starting at 0
+ *     so that it also holds the sinks, P = max(256, 16 * ceil(ceil(window_left
+ *     / 32) / 16)).
  * The grid's slot count follows from max_context_len, max_q_len and
  * min_q_len; a sequence whose q_len_b is below min_q_len is written as NaN.
  *

@@ -65,7 +65,11 @@ enum TlSlot {
 namespace ra {
 namespace {
 
-constexpr int kWaves = 8;   // waves per workgroup (two per SIMD)
+#ifndef RA_MFMA_WAVES
+#define RA_MFMA_WAVES 8
+#endif
+constexpr int kWaves = RA_MFMA_WAVES;   // waves per workgroup
+static_assert(kWaves == 8 || kWaves == 4, "8 or 4 waves per workgroup");
 constexpr int kSlab = 1024; // bytes of one wavefront-wide 16-byte load
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -89,9 +93,9 @@ struct Geo {
   // 2 .. 8 pages; NRING - 1 pages are in flight while one computes
   static constexpr int NRING_RAW = RA_MFMA_RING_KIB / NSL;
   static constexpr int NRING = NRING_RAW > 8 ? 8 : (NRING_RAW < 2 ? 2 : NRING_RAW);
-  // vector-memory operations per page: the slabs, plus one load of the
+  // vector-memory operations per page: the slabs, plus the loads of the
   // page's 16 K and 16 V scales for per-token INT8
-  static constexpr int OPS = NSL + (KV == KV_I8T ? 1 : 0);
+  static constexpr int OPS = NSL + (KV == KV_I8T ? 2 : 0);
 };
 
 template <int KV, int D>
@@ -149,8 +153,8 @@ __device__ __forceinline__ int32_t ring_page_id(IdRing& r, int32_t (*sm_id)[64],
 // straight into the LDS ring slot `ring`: one global_load_lds_dwordx4 per 1 KiB
 // slab, lane L writing bytes L*16 .. L*16+15 of the slab, the lane order the
 // cache layout has in HBM.
-// Per-token INT8 adds one load of the (page, head)'s 16 K scales (lanes 0-15)
-// and 16 V scales (lanes 16-31) into the slot's 128-byte scale area `scl`.
+// Per-token INT8 adds two 16-lane loads of the (page, head)'s 16 K scales and
+// 16 V scales into the slot's 128-byte scale area `scl`.
 // With NTP the page slabs are read with the nontemporal cache policy: a
 // launch whose units each read a page once (one row group per sequence and
 // KV head) streams its pages at about 6.8 TB/s this way against 6.1 TB/s with
@@ -163,9 +167,10 @@ __device__ __forceinline__ void issue_page(uint8_t (*ring)[kSlab], float* scl, I
   using G = Geo<KV, D>;
   const int32_t pid = ring_page_id(ids, sm_id, a, pg, ws, bt_row, i, lane, bad);
   if constexpr (KV == KV_I8T) {
-    if (lane < 32) {
-      const float* src = (lane < 16 ? a.k_scales : a.v_scales) + ((int64_t)pid * a.hkv + h) * kPage + (lane & 15);
-      __builtin_amdgcn_global_load_lds(src, (lds_u8*)scl, 4, 0, 0);
+    if (lane < 16) {   // two 16-lane loads from uniform plane bases: K scales, then V scales
+      const int64_t so = ((int64_t)pid * a.hkv + h) * kPage + lane;
+      __builtin_amdgcn_global_load_lds(a.k_scales + so, (lds_u8*)scl, 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(a.v_scales + so, (lds_u8*)(scl + 16), 4, 0, 0);
     }
   }
   const int64_t blk = ((int64_t)pid * a.hkv + h) * G::BLK;
@@ -311,32 +316,26 @@ struct Acc {
 };
 
 // Per-token INT8: take up a page's V scales into the wave's power-of-two
-// reference.  When a scale exceeds 2^7 vref the reference moves to 2^(e - 7) for
-// the page's largest scale f * 2^e (f in [0.5, 1)), and what was accumulated
-// in units of the old reference (O, and the pending page's probabilities) is
-// rescaled exactly by the ratio of the two powers of two.
+// reference.  When a scale exceeds 2^7 vref the reference moves to 2^(e - 7)
+// for the page's largest scale f * 2^e (f in [0.5, 1)).  Returns the factor,
+// old reference over new (a power of two, 0 before the first scale, 1 when
+// the reference stays), by which what was accumulated in units of the old
+// reference (O, and the pending page's probabilities) must be rescaled; the
+// softmax applies it together with its own max-refresh factor.
 template <int KV, int D, int NT>
-__device__ __forceinline__ void take_v_scales(Acc<KV, D, NT>& acc, const f32x4& vs, float (&pend)[NT][4]) {
+__device__ __forceinline__ float take_v_scales(Acc<KV, D, NT>& acc, const f32x4& vs) {
   float vm = fmaxf(fmaxf(vs[0], vs[1]), fmaxf(vs[2], vs[3]));
   vm = fmaxf(vm, __shfl_xor(vm, 16));   // the lanes' token quads: kgrp = lane bits 4, 5
   vm = fmaxf(vm, __shfl_xor(vm, 32));
   vm = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(vm)));   // (the builtin takes an int)
-  if (vm > acc.vref * 128.0f) {
-    int32_t e = (int32_t)((__float_as_uint(vm) >> 23) & 0xFFu) - 126;   // vm = f * 2^e, f in [0.5, 1)
-    e = min(max(e, -119), 120);                                         // vref and 1 / vref stay normal
-    const float nref = __uint_as_float((uint32_t)(e - 7 + 127) << 23);
-    const float ninv = __uint_as_float((uint32_t)(7 - e + 127) << 23);
-    const float f = acc.vref * ninv;                                    // old / new: a power of two, or 0
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-      for (int mt = 0; mt < Geo<KV, D>::MT; ++mt) acc.o[mt][nt] *= f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pend[nt][i] *= f;
-    }
-    acc.vref = nref;
-    acc.vinv = ninv;
-  }
+  if (!(vm > acc.vref * 128.0f)) return 1.0f;
+  int32_t e = (int32_t)((__float_as_uint(vm) >> 23) & 0xFFu) - 126;   // vm = f * 2^e, f in [0.5, 1)
+  e = min(max(e, -119), 120);                                         // vref and 1 / vref stay normal
+  const float ninv = __uint_as_float((uint32_t)(7 - e + 127) << 23);
+  const float f = acc.vref * ninv;                                    // old / new: a power of two, or 0
+  acc.vref = __uint_as_float((uint32_t)(e - 7 + 127) << 23);
+  acc.vinv = ninv;
+  return f;
 }
 
 // QK, masks and the online softmax of one page.  p receives the page's
@@ -368,8 +367,10 @@ __device__ __forceinline__ void scores_softmax(Acc<KV, D, NT>& acc, PageRegs<KV,
   // ---- masks (only on pages that can hold an invisible key).  Keys past ctx
   // (stale bytes of the last page) also get their V codes zeroed so that
   // 0 * garbage cannot produce NaN.
-  // ---- online softmax with lazy max refresh
-  const auto softmax = [&]() {
+  // ---- online softmax with lazy max refresh (per-token INT8: and with a
+  // move of the V-scale reference, fv != 1, which rescales O and the pending
+  // probabilities but not the row sums)
+  const auto softmax = [&](float fv) {
     float mx[NT];
     bool trig = false;
 #pragma unroll
@@ -378,7 +379,7 @@ __device__ __forceinline__ void scores_softmax(Acc<KV, D, NT>& acc, PageRegs<KV,
                                              __builtin_elementwise_maximum(s[nt][2], s[nt][3]));
       trig |= mx[nt] > acc.m[nt] + thr;
     }
-    if (__any(trig)) {
+    if (__any(trig) || (KV == KV_I8T && fv != 1.0f)) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         float rm = mx[nt];
@@ -391,10 +392,11 @@ __device__ __forceinline__ void scores_softmax(Acc<KV, D, NT>& acc, PageRegs<KV,
         acc.mc[nt] = acc.m[nt] == -INFINITY ? 0.0f : acc.m[nt] * c;
         if constexpr (kOnesSum<KV>) acc.ls[nt] *= alpha;
         else acc.l[nt] *= alpha;
+        const float ao = KV == KV_I8T ? alpha * fv : alpha;
 #pragma unroll
-        for (int mt = 0; mt < G::MT; ++mt) acc.o[mt][nt] *= alpha;
+        for (int mt = 0; mt < G::MT; ++mt) acc.o[mt][nt] *= ao;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pend[nt][i] *= alpha;
+        for (int i = 0; i < 4; ++i) pend[nt][i] *= ao;
       }
     }
     float vsn[4];   // per-token INT8: the V scales in units of the reference
@@ -434,8 +436,9 @@ __device__ __forceinline__ void scores_softmax(Acc<KV, D, NT>& acc, PageRegs<KV,
 #pragma unroll
       for (int w = 0; w < 4; ++w) r.v[sl][w] &= KV == KV_F16 ? ((w & 1) ? keep_hi : keep_lo) : keep8;
   }
-  if constexpr (KV == KV_I8T) take_v_scales<KV, D, NT>(acc, r.vs, pend);
-  softmax();
+  float fv = 1.0f;
+  if constexpr (KV == KV_I8T) fv = take_v_scales<KV, D, NT>(acc, r.vs);
+  softmax(fv);
 }
 
 // Fused store: quantise the unit's head's K and V rows of the query tokens
@@ -621,9 +624,18 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
   int32_t lo = 0, hi = 0;
   UnitPages pg{0, 0, 0, 0};
   if (!bad) {
-    const int32_t P = partition_tokens(a, ctx, rows);
-    lo = u.s * P;
-    hi = min(lo + P, ctx);
+    if (a.num_splits == 0 && a.window >= 0) {
+      // windowed block, automatic partitions: cut the window span from its
+      // first page; partition 0 starts at key 0 so that it also holds the sinks
+      const int32_t P = a.part_window;
+      const int32_t base = (max(fr.pmin - a.window + 1, 0) / kPage) * kPage;
+      lo = u.s == 0 ? 0 : base + u.s * P;
+      hi = min(base + (u.s + 1) * P, ctx);
+    } else {
+      const int32_t P = partition_tokens(a, ctx, rows);
+      lo = u.s * P;
+      hi = min(lo + P, ctx);
+    }
     pg = unit_pages(a, frg, lo, hi);
   }
   const int32_t npages = pg.count();
@@ -635,7 +647,8 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
   // older wave (0-3) wins issue arbitration over its partner (4-7) and runs
   // about a fifth faster, so it takes 9 of every 16 pages of the pair: both
   // then finish together.  The split depends only on the page count.
-  constexpr int32_t kFast = 9, kSlow = 16 - kFast;
+  // (With four waves, one per SIMD, the shares are equal.)
+  constexpr int32_t kFast = kWaves == 8 ? 9 : 16, kSlow = kWaves == 8 ? 16 - kFast : 16;
   const int32_t cum0 = wave < 4 ? wave * kFast : 4 * kFast + (wave - 4) * kSlow;
   const int32_t cum1 = cum0 + (wave < 4 ? kFast : kSlow);
   const int32_t p0 = (int32_t)(((int64_t)npages * cum0) >> 6), p1 = (int32_t)(((int64_t)npages * cum1) >> 6);
@@ -746,11 +759,15 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
   // are in flight; once its slab reads have retired, page k + NRING is issued
   // into the slot it freed.
   const int32_t my_pages = ws.count;
+  constexpr int NR = G::NRING;
+  uint8_t (*ring)[kSlab] = &sm_raw[wave * NR * G::NSL];
+  float* scl = &sm_scl[KV == KV_I8T ? wave * NR * 32 : 0];
+  IdRing ids{sm_id[0][lane], 0};
+#pragma unroll
+  for (int j = 0; j < NR; ++j)
+    if (j < my_pages)
+      issue_page<KV, D, NTP>(ring + j * G::NSL, scl + j * 32, ids, sm_id, a, pg, ws, j, bt_row, u.h, lane, bad);
   if (my_pages > 0) {
-    constexpr int NR = G::NRING;
-    uint8_t (*ring)[kSlab] = &sm_raw[wave * NR * G::NSL];
-    float* scl = &sm_scl[KV == KV_I8T ? wave * NR * 32 : 0];
-    IdRing ids{sm_id[0][lane], 0};
     // pages are taken in pairs for the PV product: the even page of a pair
     // waits (its masked V codes and probabilities in registers) for the odd
     // one; an odd count leaves the last page to a single-page product
@@ -763,10 +780,6 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) pend_p[nt][i] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < NR; ++j)
-      if (j < my_pages)
-        issue_page<KV, D, NTP>(ring + j * G::NSL, scl + j * 32, ids, sm_id, a, pg, ws, j, bt_row, u.h, lane, bad);
     for (int32_t i = 0; i < my_pages; i += NR) {
 #pragma unroll
       for (int j = 0; j < NR; ++j) {
@@ -809,24 +822,29 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
   wait_vmcnt<0>();   // no ring load may land after the ring becomes the merge buffer
   TL_MARK(TL_LOOP + wave);
 
+  // The lane's row and dim group, recomputed here (mbcnt) rather than kept
+  // live in registers across the page loop.
+  const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int kgrp_e = lane_e >> 4;
+  const int ncol_e = lane_e & 15;
   // ---- combine the waves.  Every wave publishes its rows' (m, l) and its
   // bad flag, then rescales its O to the common row maximum.
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     float l;
     if constexpr (kOnesSum<KV>) {
-      l = acc.ls[nt][0];   // the whole row's sum in every lane of the row
+      l = acc.ls[nt][0];   // the whole row's sum in every lane_e of the row
     } else {
       l = acc.l[nt];
       l += __shfl_xor(l, 16);
       l += __shfl_xor(l, 32);
     }
-    if (kgrp == 0) {
-      reinterpret_cast<float*>(&sm_ml[0][nt * 16 + ncol][0])[wave] = acc.m[nt];
-      reinterpret_cast<float*>(&sm_ml[1][nt * 16 + ncol][0])[wave] = l;
+    if (kgrp_e == 0) {
+      reinterpret_cast<float*>(&sm_ml[0][nt * 16 + ncol_e][0])[wave] = acc.m[nt];
+      reinterpret_cast<float*>(&sm_ml[1][nt * 16 + ncol_e][0])[wave] = l;
     }
   }
-  if (lane == 0) sm_bad[wave] = bad ? 1 : 0;
+  if (lane_e == 0) sm_bad[wave] = bad ? 1 : 0;
   __syncthreads();
   if (wave == 0) TL_MARK(TL_COMB);
 #pragma unroll
@@ -834,7 +852,7 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
   float Mrow[NT], Lrow[NT], fself[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const int rr = nt * 16 + ncol;
+    const int rr = nt * 16 + ncol_e;
     float mw[kWaves], lw[kWaves];
 #pragma unroll
     for (int q = 0; q < kWaves / 4; ++q) {
@@ -862,12 +880,12 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
   }
   if (wave == 0) TL_MARK(TL_ML);
 
-  // ---- reduce-scatter of O through LDS, in two passes over the lane's
-  // accumulator components i (pass p: i = 2p, 2p + 1).  The lane's values
-  // acc.o[0..MT)[nt][i] are the MT consecutive dims (4 kgrp + i) * MT .. + MT of
-  // row nt * 16 + ncol; every wave stores them, then wave w < 2 NT sums pair
+  // ---- reduce-scatter of O through LDS, in two passes over the lane_e's
+  // accumulator components i (pass p: i = 2p, 2p + 1).  The lane_e's values
+  // acc.o[0..MT)[nt][i] are the MT consecutive dims (4 kgrp_e + i) * MT .. + MT of
+  // row nt * 16 + ncol_e; every wave stores them, then wave w < 2 NT sums pair
   // w = (nt, i) over the waves in wave order and writes that slice of the
-  // output (same lanes, so the row and its (M, L) are the lane's own).
+  // output (same lanes, so the row and its (M, L) are the lane_e's own).
   f32x4* red = reinterpret_cast<f32x4*>(&sm_raw[0][0]);   // [kPairs][kWaves][MT / 4][kWave]
   const float vs = a.v_scale;
 #pragma unroll
@@ -875,7 +893,7 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
 #pragma unroll
     for (int pr = 0; pr < kPairs; ++pr) {
       const int nt = pr >> 1, i = 2 * p + (pr & 1);
-      f32x4* dst = red + (pr * kWaves + wave) * (G::MT / 4) * kWave + lane;
+      f32x4* dst = red + (pr * kWaves + wave) * (G::MT / 4) * kWave + lane_e;
 #pragma unroll
       for (int k = 0; k < G::MT / 4; ++k)
         dst[k * kWave] =
@@ -884,15 +902,14 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
     }
     __syncthreads();
     if (wave == 0) TL_MARK(TL_P0W + p);
-    if (wave < kPairs) {
-      const int pr = wave;
+    for (int pr = wave; pr < kPairs; pr += kWaves) {
       const int nt = pr >> 1, i = 2 * p + (pr & 1);
       float v[G::MT];
 #pragma unroll
       for (int mt = 0; mt < G::MT; ++mt) v[mt] = 0.0f;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const f32x4* src = red + (pr * kWaves + w) * (G::MT / 4) * kWave + lane;
+        const f32x4* src = red + (pr * kWaves + w) * (G::MT / 4) * kWave + lane_e;
 #pragma unroll
         for (int k = 0; k < G::MT / 4; ++k) {
           const f32x4 x = src[k * kWave];
@@ -900,19 +917,19 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
           for (int j = 0; j < 4; ++j) v[4 * k + j] += x[j];
         }
       }
-      // rows of this pair, by the lane's own (M, L)
+      // rows of this pair, by the lane_e's own (M, L)
       float L = 0.0f, M = 0.0f;
 #pragma unroll
       for (int t = 0; t < NT; ++t)
         if (t == nt) { L = Lrow[t]; M = Mrow[t]; }
-      const int32_t r = row0 + nt * 16 + ncol;
+      const int32_t r = row0 + nt * 16 + ncol_e;
       if (r < rows) {
         const int32_t qi = r / g, hj = r % g;
         const int64_t orow = (int64_t)(q0 + qi) * a.hq + u.h * g + hj;
         // a row with no visible key has L = 0 (out 0, lse -inf); NaN scores
         // leave L = NaN, and the row stays NaN in out and lse
         const float inv = L > 0.0f ? vs / L : (L == L ? 0.0f : __builtin_nanf(""));
-        const int d0 = (4 * kgrp + i) * G::MT;
+        const int d0 = (4 * kgrp_e + i) * G::MT;
 #pragma unroll
         for (int mt = 0; mt < G::MT; ++mt) v[mt] = bad ? __builtin_nanf("") : v[mt] * inv;
         if (a.direct) {
@@ -939,7 +956,7 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
           for (int k = 0; k < G::MT / 4; ++k)
             *reinterpret_cast<f32x4*>(op + 4 * k) = f32x4{v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]};
         }
-        if (kgrp == 0 && i == 0) {
+        if (kgrp_e == 0 && i == 0) {
           float lse = L > 0.0f ? (M * c + log2f(L)) * kLn2 : (L == L ? -INFINITY : __builtin_nanf(""));
           if (bad) lse = __builtin_nanf("");
           if (a.direct) {

@@ -128,6 +128,12 @@ int32_t check_attn(const ra_attn_args* a, Plan* plan) {
                              : ceil_div(c, plan->part_large);
       s = std::max<int64_t>(s, sm);
     }
+    if (a->window_left >= 0) {
+      // windowed blocks: partitions over the window span (from its first
+      // page: up to 15 keys before it) plus, in partition 0, the sinks
+      const int64_t span = std::min<int64_t>(a->max_context_len, (int64_t)a->window_left + a->max_q_len + 14);
+      s = std::max<int64_t>(1, ceil_div(span, ra::window_partition_tokens(a->window_left)));
+    }
     if (s > RA_KV_MAX_SPLITS * 64)
       return fail(RA_ERR_INVALID_ARG, "ra_paged_attn: max_context_len %d needs too many partitions",
                   a->max_context_len);
@@ -379,6 +385,7 @@ int32_t ra_paged_attn(const ra_attn_args* args, void* stream) {
   hipError_t e = hipSuccess;
   L.part_tokens = p.part_large;
   L.part_small = p.part_small;
+  L.part_window = args->window_left >= 0 ? ra::window_partition_tokens(args->window_left) : 0;
   // long query blocks (more than kPrefillMinRows rows per KV head) go to the
   // prefill kernel when the call's constants allow; the decode kernel's grid
   // then covers only the shorter blocks

@@ -107,6 +107,7 @@ struct AttnLaunch {
   int32_t slots;         // partition slots per sequence in the grid
   int32_t part_tokens;   // auto mode: partition size (tokens) of units with >= kSmallUnitRows rows
   int32_t part_small;    // auto mode: partition size of units with fewer rows
+  int32_t part_window;   // auto mode with a window: partition size over the window span
   bool direct;           // write out/lse directly (one slot)
   float* k_scales;       // KV_I8T scale planes [num_pages][hkv][16] (written by the fused store)
   float* v_scales;
@@ -141,11 +142,28 @@ constexpr int kMfmaRowsPerBlock = 48;   // rows beyond this split over row group
 // [kAutoPartSmall, kAutoPartLarge] tokens, so that a decode batch still fills
 // the chip while long contexts keep few partials.  Either rule depends only on
 // the sequence itself, never on the rest of the batch.
+#ifndef RA_AUTO_PART_LARGE
+#define RA_AUTO_PART_LARGE 2048
+#endif
 constexpr int kSmallUnitRows = 16;
-constexpr int kAutoPartLarge = 2048;
+constexpr int kAutoPartLarge = RA_AUTO_PART_LARGE;
 constexpr int kAutoPartSmall = 512;
 constexpr int kSmallSplits = 32;
 constexpr int kFillUnits = 2048;
+// Automatic partitions of a windowed block (window_left >= 0): only the sinks
+// and the window span [pmin - W + 1, pmax] of the block hold visible keys, so
+// the partitions cut that span, from its first page on, instead of [0, ctx):
+// partition s covers [base + s P, base + (s + 1) P), base the first page of
+// the span, and partition 0 also takes the sink keys below base.  P depends
+// only on the window: about kWindowSplits partitions of a window, at least
+// kAutoPartWindow tokens each.
+constexpr int kAutoPartWindow = 256;
+constexpr int kWindowSplits = 32;
+__host__ __device__ inline int32_t window_partition_tokens(int32_t window) {
+  const int32_t per = (window + kWindowSplits - 1) / kWindowSplits;
+  const int32_t p = ((per + 15) / 16) * 16;
+  return p > kAutoPartWindow ? p : kAutoPartWindow;
+}
 
 hipError_t launch_attn_mfma(const AttnLaunch& a, hipStream_t s);
 

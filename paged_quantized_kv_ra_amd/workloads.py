@@ -357,6 +357,15 @@ def split_fp8_512k_sliding(base=None):
                  num_sinks=4, kv_source=base)
 
 
+def split_fp8_512k_sliding_auto(base=None):
+    """The sliding-window variant with automatic partitions (num_splits = 0),
+    which cut the window span instead of the whole 512K context."""
+    return build("split_e4m3_2x512k_q16_w4096_sink4_auto", 4, ctx=[512 * K] * 2, q_len=16,
+                 num_q_heads=16, num_kv_heads=2, head_dim=128, kv_dtype="e4m3",
+                 q_dtype="f16", pool_pages=65536, num_splits=0, window_left=4096,
+                 num_sinks=4, kv_source=base)
+
+
 def prefill_fp8_8k():
     """Cold prefill of an 8K prompt: one sequence whose 8,192 tokens are all
     queries, causal, E4M3 KV (ReVolta README, intro table, "Cold prompt 8K
@@ -387,6 +396,7 @@ BENCH_WORKLOADS = {
     "prefix_int8_256k": prefix_int8_256k,
     "split_fp8_512k": split_fp8_512k,
     "split_fp8_512k_sliding": split_fp8_512k_sliding,
+    "split_fp8_512k_sliding_auto": split_fp8_512k_sliding_auto,
     "prefill_fp8_8k": prefill_fp8_8k,
     "chunk_prefill_fp8_128k": chunk_prefill_fp8_128k,
 }

@@ -126,3 +126,4 @@ def test_benchmark_workload(cfg):
 def test_sliding_window_workload():
     base = W.split_fp8_512k()
     _run("split_fp8_512k_sliding", W.split_fp8_512k_sliding, "all", base=base)
+    _run("split_fp8_512k_sliding_auto", W.split_fp8_512k_sliding_auto, "all", base=base)
