@@ -250,36 +250,72 @@ class Step:
             raise RuntimeError(lib.ra_last_error().decode())
 
 
-def algorithmic_bytes(w):
+def algorithmic_bytes(w, unique=False):
     """HBM bytes one attention launch must move: the visible KV tokens' codes
     (2 * Hkv * D * e per token, plus 2 * Hkv * 4 B of scales for per-token
     INT8), the block-table entries of the visited pages
     (4 B per 16 tokens per sequence), the queries read and the output and
-    its lse written (partials are the implementation's own traffic)."""
+    its lse written (partials are the implementation's own traffic).  With
+    unique=True the KV bytes count every physical page once (pages shared by
+    several sequences' block tables are read from HBM once at best)."""
     kv = w.kv_bytes_attended()
+    if unique and w.window_left < 0:
+        per_tok = w.kv_bytes_attended() / max(1, w.attended_keys())
+        kv = int(round(per_tok * 16 * w.unique_pages_attended()))
     bt = 4 * sum(-(-int(c) // 16) for c in w.ctx)
     q = w.q.nbytes
     out = w.q.nbytes + 4 * w.total_q * w.num_q_heads
     return kv + bt + q + out
 
 
+def host_cores():
+    """Cores this process may use: its CPU affinity, capped by OMP_NUM_THREADS
+    when that is set (the host's share of cores for one GPU)."""
+    n = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, n)
+
+
 def cpu_baseline(w, seconds):
-    """The oracle (numpy, fp64) on whole sequences of the same step, until
-    about `seconds` of CPU time: dequantise the cached codes, then attend."""
+    """The oracle (numpy, fp64, BLAS for the products) on whole sequences of
+    the same step: dequantise the cached codes, then attend.  Timed at one
+    BLAS thread and at all of the host's cores, each the median of 3 runs of
+    about seconds / 6 of CPU work; `value` is the all-cores median."""
+    from threadpoolctl import threadpool_limits
     sys.path.insert(0, ROOT)
     from oracle import attention as OA
     from oracle import codecs as OC
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = 1
+    cores = host_cores()
+    per_run = max(0.5, seconds / 6.0)
+    codes = {}          # the cache contents per sequence: made once, not timed
+    res = {}
+    for threads in (1, cores):
+        runs = []
+        with threadpool_limits(limits=threads):
+            for _ in range(3):
+                if w.meta.get("kind") == "prefill":
+                    runs.append(cpu_baseline_prefill(w, per_run, threads, OA, OC))
+                else:
+                    runs.append(_cpu_decode_run(w, per_run, threads, OA, OC, codes))
+        runs.sort(key=lambda r: r["value"])
+        res[threads] = runs
+    med = res[cores][1]
+    one = res[1][1]
+    return {"value": med["value"], "unit": med["unit"], "cores": cores, "kind": "oracle",
+            "sample": med["sample"] + f"; median of 3 runs at {cores} BLAS threads",
+            "runs_value": [round(r["value"], 1) for r in res[cores]],
+            "single_thread": {"value": one["value"], "unit": one["unit"], "cores": 1,
+                              "runs_value": [round(r["value"], 1) for r in res[1]], "sample": one["sample"]}}
+
+
+def _cpu_decode_run(w, seconds, threads, OA, OC, codes):
+    """One timed run of the oracle on whole sequences until about `seconds`
+    (`codes`: the sequences' cached codes, shared between runs)."""
     g = w.num_q_heads // w.num_kv_heads
-    if w.meta.get("kind") == "prefill":
-        return cpu_baseline_prefill(w, seconds, threads, OA, OC)
     done_tokens, elapsed, seqs = 0, 0.0, 0
     b = 0
-    codes = {}
     while elapsed < seconds and seqs < 64 * w.batch:
         if b % w.batch not in codes:       # the cache contents: made once, not timed
             rows = w.seq_rows[b % w.batch]
@@ -394,7 +430,38 @@ def time_graphs(step, args, torch):
     a1.record()
     torch.cuda.synchronize()
     attn_avg_ms = a0.elapsed_time(a1) / (reps * step.copies)
+    step.graphs = step_graphs
     return ms_per_step, attn_avg_ms, wall
+
+
+def launch_percentiles(step, args, torch, n=200):
+    """Per-launch times: n attention launches, each bracketed by its own pair
+    of HIP events on the launch stream (eager, one pool copy after another),
+    and n graph-replayed steps, each bracketed the same way.  us."""
+    import numpy as np
+    sp = torch.cuda.current_stream().cuda_stream
+    mk = (lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
+    ev = [mk() for _ in range(n)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        ev[i][0].record()
+        step.run_attention(i, sp)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    attn = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    out = {"attn_us": {k: round(float(np.percentile(attn, q)), 2) for k, q in (("p10", 10), ("median", 50),
+                                                                               ("p90", 90))}}
+    if getattr(step, "graphs", None):
+        ev = [mk() for _ in range(n)]
+        for i in range(n):
+            ev[i][0].record()
+            step.graphs[i % len(step.graphs)].replay()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        st = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+        out["step_us"] = {k: round(float(np.percentile(st, q)), 2) for k, q in (("p10", 10), ("median", 50),
+                                                                              ("p90", 90))}
+    return out
 
 
 def time_eager(step, args, torch):
@@ -517,8 +584,9 @@ def timeline(step, args, torch):
         us = 1e-2                                     # 100 MHz ticks
         entry = t[:, TL["entry"]]
         t0 = entry.min()
-        loops = t[:, TL["loop"]:TL["loop"] + 8]
-        ends = t[:, TL["end"]:TL["end"] + 8]
+        nw = int((t[:, TL["loop"]:TL["loop"] + 8] > 0).sum(axis=1).max())   # waves per workgroup
+        loops = t[:, TL["loop"]:TL["loop"] + nw]
+        ends = t[:, TL["end"]:TL["end"] + nw]
         end = ends.max(axis=1)
         acc["start"] += list((entry - t0) * us)
         acc["meta"] += list((t[:, TL["meta"]] - entry) * us)
@@ -555,8 +623,8 @@ def timeline(step, args, torch):
 
 def main():
     args = parse()
-    if args.timeline:   # the timing build of the library (same ABI)
-        os.environ["RA_KV_LIB"] = os.path.join(ROOT, "paged_quantized_kv_ra_amd", "libra_kv_timeline.so")
+    if args.timeline:   # the timing build of the library (same ABI), unless another one is named
+        os.environ.setdefault("RA_KV_LIB", os.path.join(ROOT, "paged_quantized_kv_ra_amd", "libra_kv_timeline.so"))
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this path is single-GPU "
               "by design and has no multi-GPU mode.", file=sys.stderr)
@@ -592,6 +660,7 @@ def main():
     tflops = flops / (attn_avg_ms / 1e3) / 1e12
     src_hash = kernel_source_hash()
     traffic = traffic_from_profile(w.name, src_hash)
+    pct = launch_percentiles(step, args, torch)
     log(f"{args.steps} steps ({'eager' if args.eager else 'graph replay'}): {ms_per_step * 1e3:.1f} us/step "
         f"(wall {wall / args.steps * 1e6:.1f} us/step), "
         f"attention {attn_avg_ms * 1e3:.1f} us avg, {achieved:.0f} GB/s algorithmic, {tflops:.1f} TFLOP/s")
@@ -608,6 +677,14 @@ def main():
                 "traffic": traffic, "kernel": "attn_mfma_kernel",
                 "algorithmic_bytes_per_launch": alg, "attn_us": round(attn_avg_ms * 1e3, 2),
                 "kernel_source_hash": src_hash}
+        # HBM bytes the counters saw per launch over the same average time
+        roof["hbm_gbs"] = round(traffic / (attn_avg_ms / 1e3) / 1e9, 1) if traffic else None
+        uniq = algorithmic_bytes(w, unique=True)
+        if uniq != alg:   # pages shared between sequences (prefix caching): the bytes counted once
+            roof["algorithmic_bytes_unique_per_launch"] = uniq
+            roof["achieved_unique"] = round(uniq / (attn_avg_ms / 1e3) / 1e9, 1)
+            roof["frac_unique"] = round(uniq / (attn_avg_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4)
+    roof.update({"attn_us_" + k: v for k, v in pct["attn_us"].items()})
     line = {
         "metric": ("prefill query tokens/sec (paged attention, one layer), FP8 KV" if prefill else
                    "KV tokens attended/sec and achieved HBM GB/s (% of MI355X peak), FP8 KV @32K"),
@@ -631,6 +708,8 @@ def main():
         "roofline": roof,
         "attended_tokens_per_step": tokens,
     }
+    if "step_us" in pct:
+        line["step_us_percentiles"] = pct["step_us"]
     if not args.no_cpu_baseline:
         log("timing the CPU oracle sample ...")
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -50,6 +50,16 @@ def test_algorithmic_bytes_window_and_sinks():
     assert bench.algorithmic_bytes(w) == kv_bytes + table + q_bytes + q_bytes + 16 * 4 * 4
 
 
+def test_unique_bytes_count_shared_prefix_pages_once():
+    # 3 sequences of 100 keys whose first 64 keys (4 pages) share physical
+    # pages: 4 shared + 3 x 3 private pages hold all visible keys
+    w = W.build("t", 5, ctx=[100] * 3, q_len=1, num_q_heads=2, num_kv_heads=1, head_dim=64, kv_dtype="int8",
+                shared_prefix_tokens=64)
+    per_token = 2 * 1 * 64
+    base = bench.algorithmic_bytes(w) - 300 * per_token
+    assert bench.algorithmic_bytes(w, unique=True) == base + (4 + 3 * 3) * 16 * per_token
+
+
 @pytest.mark.gpu
 def test_bench_json_line():
     print("bench.py --workload tiny_decode --steps 5 --warmup 2 --cpu-seconds 0.5", flush=True)
@@ -68,5 +78,14 @@ def test_bench_json_line():
     roof = j["roofline"]
     assert roof["bound"] == "hbm" and roof["peak"] == 8000.0 and roof["unit"] == "GB/s"
     assert roof["achieved"] > 0 and abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
+    for k in ("attn_us_p10", "attn_us_median", "attn_us_p90"):
+        assert roof[k] > 0, k
+    assert roof["attn_us_p10"] <= roof["attn_us_median"] <= roof["attn_us_p90"]
+    assert "hbm_gbs" in roof
+    st = j["step_us_percentiles"]
+    assert 0 < st["p10"] <= st["median"] <= st["p90"]
     cb = j["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
+    assert len(cb["runs_value"]) == 3 and sorted(cb["runs_value"])[1] == round(cb["value"], 1)
+    one = cb["single_thread"]
+    assert one["cores"] == 1 and one["value"] > 0 and len(one["runs_value"]) == 3
