@@ -122,6 +122,21 @@ struct WaveSpan {
   __device__ __forceinline__ int32_t page(int32_t k) const { return first + stride * k; }
 };
 
+// The lane's entry of an id chunk that LDS DMA wrote: read from assembly (and
+// waited for in the same block), because for an ordinary LDS read the compiler
+// would first wait for every outstanding DMA of the wave, page loads and
+// query rows included; the caller's vmcnt wait retires the chunk's DMA.
+__device__ __forceinline__ int32_t read_id(const int32_t* slot, int lane) {
+  int32_t v;
+  asm volatile(
+      "ds_read_b32 %0, %1\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(v)
+      : "v"((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) int32_t*)(slot + lane))
+      : "memory");
+  return v;
+}
+
 __device__ __forceinline__ void id_dma(int32_t* slot, const UnitPages& pg, const WaveSpan& ws, const int32_t* bt_row,
                                        int32_t chunk, int lane) {
   const int32_t k = chunk * 64 + lane;
@@ -138,7 +153,7 @@ __device__ __forceinline__ int32_t ring_page_id(IdRing& r, int32_t (*sm_id)[64],
   const int32_t ch = k >> 6;
   if (ch != r.chunk) {       // wave-uniform, once per 64 pages
     r.chunk = ch;
-    r.cur = sm_id[ch & 1][lane];
+    r.cur = read_id(sm_id[ch & 1], lane);
     id_dma(sm_id[(ch + 1) & 1], pg, ws, bt_row, ch + 1, lane);
   }
   int32_t id = __builtin_amdgcn_readlane(r.cur, k & 63);
@@ -676,8 +691,31 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
   // the fused store of the query tokens' own K/V (decode and verify blocks)
   bool stored = false;
   if (a.new_k != nullptr && !bad) stored = store_new_tokens<KV, D>(a, u.h, q0, q_len, fr.pmin, lo, hi);
-  wait_vmcnt<0>();   // the first id chunks and the query rows have landed, and the stores have completed
-  if (stored) __syncthreads();   // before any wave's page loads can read a stored token
+  const int32_t my_pages = ws.count;
+  constexpr int NR = G::NRING;
+  uint8_t (*ring)[kSlab] = &sm_raw[wave * NR * G::NSL];
+  float* scl = &sm_scl[KV == KV_I8T ? wave * NR * 32 : 0];
+  // Without a store or RoPE here, the first ring pages are requested as soon
+  // as the page ids have landed, and the query rows (requested after the
+  // ids, so that waiting for the ids leaves them in flight) arrive meanwhile.
+  const bool early = !stored && a.rope == nullptr;
+  IdRing ids{0, 0};
+  if (early) {
+    wait_vmcnt<NT * G::KS>();   // the id chunks, older than the NT * KS query loads, have landed
+    ids.cur = read_id(sm_id[0], lane);
+#pragma unroll
+    for (int j = 0; j < NR; ++j)
+      if (j < my_pages)
+        issue_page<KV, D, NTP>(ring + j * G::NSL, scl + j * 32, ids, sm_id, a, pg, ws, j, bt_row, u.h, lane, bad);
+    // the query rows, older than the pages just requested
+    if (my_pages >= NR)
+      wait_vmcnt<NR * G::OPS>();
+    else
+      wait_vmcnt<0>();
+  } else {
+    wait_vmcnt<0>();   // the first id chunks and the query rows have landed, and the stores have completed
+    if (stored) __syncthreads();   // before any wave's page loads can read a stored token
+  }
   if (wave == 0) {
     TL_MARK(TL_IDSQ);
     TL_VALUE(TL_PAGES, npages);
@@ -758,15 +796,13 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
   // ring: page k computes from slot k % NRING while pages k + 1 .. k + NRING - 1
   // are in flight; once its slab reads have retired, page k + NRING is issued
   // into the slot it freed.
-  const int32_t my_pages = ws.count;
-  constexpr int NR = G::NRING;
-  uint8_t (*ring)[kSlab] = &sm_raw[wave * NR * G::NSL];
-  float* scl = &sm_scl[KV == KV_I8T ? wave * NR * 32 : 0];
-  IdRing ids{sm_id[0][lane], 0};
+  if (!early) {
+    ids.cur = read_id(sm_id[0], lane);
 #pragma unroll
-  for (int j = 0; j < NR; ++j)
-    if (j < my_pages)
-      issue_page<KV, D, NTP>(ring + j * G::NSL, scl + j * 32, ids, sm_id, a, pg, ws, j, bt_row, u.h, lane, bad);
+    for (int j = 0; j < NR; ++j)
+      if (j < my_pages)
+        issue_page<KV, D, NTP>(ring + j * G::NSL, scl + j * 32, ids, sm_id, a, pg, ws, j, bt_row, u.h, lane, bad);
+  }
   if (my_pages > 0) {
     // pages are taken in pairs for the PV product: the even page of a pair
     // waits (its masked V codes and probabilities in registers) for the odd
