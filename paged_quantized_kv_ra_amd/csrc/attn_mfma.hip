@@ -137,6 +137,33 @@ __device__ __forceinline__ int32_t read_id(const int32_t* slot, int lane) {
   return v;
 }
 
+// The KS query operands of one 16-row tile (1 KiB apart in LDS), read from
+// assembly and waited for in the same block, for the reason given above.
+template <int KS>
+__device__ __forceinline__ void read_q_tile(const void* base, u32x4 (&w)[KS]) {
+  const uint32_t adr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)base;
+  if constexpr (KS == 4) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %4 offset:1024\n\t"
+        "ds_read_b128 %2, %4 offset:2048\n\t"
+        "ds_read_b128 %3, %4 offset:3072\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3])
+        : "v"(adr)
+        : "memory");
+  } else {
+    static_assert(KS == 2, "two or four k-steps");
+    asm volatile(
+        "ds_read_b128 %0, %2\n\t"
+        "ds_read_b128 %1, %2 offset:1024\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(w[0]), "=&v"(w[1])
+        : "v"(adr)
+        : "memory");
+  }
+}
+
 __device__ __forceinline__ void id_dma(int32_t* slot, const UnitPages& pg, const WaveSpan& ws, const int32_t* bt_row,
                                        int32_t chunk, int lane) {
   const int32_t k = chunk * 64 + lane;
@@ -673,20 +700,37 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
   const uint32_t lane_off = (uint32_t)lane * 16u;
 
   // query fragments: lane (kgrp, ncol) holds row ncol of each 16-row tile,
-  // dims kgrp * D/4 + 8 * ks .. + 8.  Every wave loads its own copy, in
-  // flight together with the id DMA, and keeps it in registers.
+  // dims kgrp * D/4 + 8 * ks .. + 8.  The workgroup loads the tile once, by
+  // LDS DMA straight into operand order (one instruction per (tile, k-step)
+  // fills a 1 KiB slab, lane L's 16 bytes at L * 16), in flight together with
+  // the id DMA; the instructions are spread over the waves, each wave issuing
+  // the same number kQOps of them (some issued twice, writing the same bytes)
+  // so that its wait counts are exact.  (RoPE on the fused path rotates the
+  // tile into the same slabs instead.)
+  constexpr int kQInst = NT * G::KS;
+  constexpr int kQOps = (kQInst + kWaves - 1) / kWaves;
   int32_t pos[NT];
-  u32x4 qraw[NT][G::KS];
   bool qlive[NT];
+  const uint16_t* qp[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int32_t r = row0 + nt * 16 + ncol;
     qlive[nt] = r < rows && !bad;
     pos[nt] = fr.pmin + (qlive[nt] ? r / g : 0);
     const int64_t qtok = qlive[nt] ? q0 + r / g : 0, qhead = qlive[nt] ? u.h * g + r % g : 0;
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + qtok * a.q_stride + qhead * D + kgrp * (D / 4);
+    qp[nt] = reinterpret_cast<const uint16_t*>(a.q) + qtok * a.q_stride + qhead * D + kgrp * (D / 4);
+  }
+  if (a.rope == nullptr) {
 #pragma unroll
-    for (int ks = 0; ks < G::KS; ++ks) qraw[nt][ks] = load16(qp + 8 * ks);
+    for (int j = 0; j < kQOps; ++j) {
+      const int i = (wave + j * kWaves) % kQInst;   // uniform
+      const int qt = i / G::KS, ks = i % G::KS;
+      const uint16_t* src = qp[0];
+#pragma unroll
+      for (int t = 1; t < NT; ++t)
+        if (qt == t) src = qp[t];
+      __builtin_amdgcn_global_load_lds(src + 8 * ks, (lds_u8*)&sm_q[qt][ks][0], 16, 0, 0);
+    }
   }
   // the fused store of the query tokens' own K/V (decode and verify blocks)
   bool stored = false;
@@ -701,20 +745,24 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
   const bool early = !stored && a.rope == nullptr;
   IdRing ids{0, 0};
   if (early) {
-    wait_vmcnt<NT * G::KS>();   // the id chunks, older than the NT * KS query loads, have landed
+    wait_vmcnt<kQOps>();   // the id chunks, older than this wave's kQOps query loads, have landed
     ids.cur = read_id(sm_id[0], lane);
 #pragma unroll
     for (int j = 0; j < NR; ++j)
       if (j < my_pages)
         issue_page<KV, D, NTP>(ring + j * G::NSL, scl + j * 32, ids, sm_id, a, pg, ws, j, bt_row, u.h, lane, bad);
-    // the query rows, older than the pages just requested
+    // this wave's query loads, older than the pages just requested; then
+    // every wave's (a plain barrier: the pages stay in flight)
     if (my_pages >= NR)
       wait_vmcnt<NR * G::OPS>();
     else
       wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
   } else {
-    wait_vmcnt<0>();   // the first id chunks and the query rows have landed, and the stores have completed
-    if (stored) __syncthreads();   // before any wave's page loads can read a stored token
+    // the first id chunks and the query rows have landed and the stores have
+    // completed, in every wave: no page load can read a stored token before
+    wait_vmcnt<0>();
+    __syncthreads();
   }
   if (wave == 0) {
     TL_MARK(TL_IDSQ);
@@ -724,9 +772,11 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
   if (a.rope == nullptr) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
+      u32x4 qraw[G::KS];
+      read_q_tile<G::KS>(&sm_q[nt][0][lane], qraw);
 #pragma unroll
       for (int ks = 0; ks < G::KS; ++ks) {
-        const u32x4 w = qlive[nt] ? qraw[nt][ks] : u32x4{0, 0, 0, 0};
+        const u32x4 w = qlive[nt] ? qraw[ks] : u32x4{0, 0, 0, 0};
         if (a.q_bf16) {
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
