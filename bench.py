@@ -79,6 +79,8 @@ def parse():
                     help="per-workgroup phase timings of the attention kernel, from the timing build "
                          "libra_kv_timeline.so (python -m paged_quantized_kv_ra_amd.build --timeline)")
     ap.add_argument("--timeline-launches", type=int, default=20)
+    ap.add_argument("--timeline-dump", default=None,
+                    help="with --timeline: also save every launch's raw per-workgroup slots (numpy .npy, int64 ticks)")
     ap.add_argument("--read-ceiling", action="store_true",
                     help="HBM read rate of random 2/4/8 KiB blocks read the way the attention reads pages "
                          "(libra_probe.so), against a streaming read")
@@ -559,16 +561,16 @@ def timeline(step, args, torch):
     lib.ra_timeline_layout(ctypes.byref(nb), ctypes.byref(ns))
     nb, ns = nb.value, ns.value
     TL = dict(entry=0, hwid=1, xcc=2, meta=3, idsq=4, first=5, pages=6, loop=8, comb=16, ml=17, p0w=18, p1w=19,
-              p0r=20, p1r=21, end=24)
+              p0r=20, p1r=21, end=24, plan=32, idiss=33, idland=34, pgiss=35)
     sp = torch.cuda.current_stream().cuda_stream
     for i in range(args.warmup):
         step.run(i, sp)
     torch.cuda.synchronize()
     buf = np.zeros(nb * ns, dtype=np.uint64)
-    acc = {k: [] for k in ("start", "meta", "idsq", "first", "stream_wave_median", "wave_skew", "combine",
+    acc = {k: [] for k in ("start", "meta", "plan", "ids_issued", "ids_landed", "pages_issued", "idsq", "first", "stream_wave_median", "wave_skew", "combine",
                            "comb_barrier1", "comb_row_stats", "comb_pass0_write", "comb_pass0_reduce",
                            "comb_pass1_write", "comb_pass1_reduce", "comb_tail", "block", "end_after_median")}
-    spans, blocks_per_cu = [], []
+    spans, blocks_per_cu, raw = [], [], []
     for i in range(args.timeline_launches):
         if lib.ra_timeline_clear() != 0:
             raise RuntimeError("ra_timeline_clear failed")
@@ -581,6 +583,8 @@ def timeline(step, args, torch):
         t = t[live]
         if t.shape[0] == 0:
             continue
+        if args.timeline_dump:
+            raw.append(np.concatenate([np.full((t.shape[0], 1), i, dtype=np.int64), t], axis=1))
         us = 1e-2                                     # 100 MHz ticks
         entry = t[:, TL["entry"]]
         t0 = entry.min()
@@ -590,6 +594,9 @@ def timeline(step, args, torch):
         end = ends.max(axis=1)
         acc["start"] += list((entry - t0) * us)
         acc["meta"] += list((t[:, TL["meta"]] - entry) * us)
+        for k, slot in (("plan", "plan"), ("ids_issued", "idiss"), ("ids_landed", "idland"), ("pages_issued", "pgiss")):
+            ok = t[:, TL[slot]] > 0
+            acc[k] += list((t[ok, TL[slot]] - entry[ok]) * us)
         acc["idsq"] += list((t[:, TL["idsq"]] - entry) * us)
         acc["first"] += list((t[:, TL["first"]] - entry) * us)
         acc["stream_wave_median"] += list((np.median(loops, axis=1) - t[:, TL["first"]]) * us)
@@ -609,6 +616,8 @@ def timeline(step, args, torch):
         cu = (t[:, TL["xcc"]] & 0xF) * 4096 + ((hw >> 13) & 0x7) * 512 + ((hw >> 12) & 1) * 256 + ((hw >> 8) & 0xF)
         _, counts = np.unique(cu, return_counts=True)
         blocks_per_cu.append((len(counts), float(counts.mean()), int(counts.max())))
+    if args.timeline_dump and raw:
+        np.save(args.timeline_dump, np.concatenate(raw, axis=0))   # columns: launch, then the slots
     res = {"workload": step.w.name, "launches": len(spans), "kernel_span_us": _pct(spans),
            "cus_used": blocks_per_cu[-1][0] if blocks_per_cu else None,
            "blocks_per_cu_max": max(b[2] for b in blocks_per_cu) if blocks_per_cu else None,

@@ -25,6 +25,9 @@
 
 namespace ra {
 
+// floor(n / f.d) for 0 <= n < 2^31 (fastdiv.h)
+__device__ __forceinline__ uint32_t fdiv(const FastDiv& f, uint32_t n) { return (__umulhi(n, f.m) + n) >> f.l; }
+
 struct UnitPages {
   int32_t p0a, na;   // first page and count of the first page range
   int32_t p0b, nb;   // second range (window pages when a sink range exists)
@@ -118,10 +121,15 @@ __device__ __forceinline__ bool decode_unit(const AttnLaunch& a, int32_t row_gro
   const uint32_t total = (uint32_t)a.slots * (uint32_t)a.hkv * (uint32_t)row_groups * (uint32_t)a.batch;
   uint32_t id = logical_block(total, row_groups);
   if (id >= total) return false;
-  u.b = (int32_t)(id % (uint32_t)a.batch); id /= (uint32_t)a.batch;
-  u.h = (int32_t)(id % (uint32_t)a.hkv); id /= (uint32_t)a.hkv;
-  u.rg = row_groups - 1 - (int32_t)(id % (uint32_t)row_groups); id /= (uint32_t)row_groups;
-  u.s = (int32_t)id;
+  uint32_t q = fdiv(a.fd_batch, id);
+  u.b = (int32_t)(id - q * (uint32_t)a.batch);
+  id = q;
+  q = fdiv(a.fd_hkv, id);
+  u.h = (int32_t)(id - q * (uint32_t)a.hkv);
+  id = q;
+  q = fdiv(a.fd_rg, id);
+  u.rg = row_groups - 1 - (int32_t)(id - q * (uint32_t)row_groups);
+  u.s = (int32_t)q;
   return true;
 }
 

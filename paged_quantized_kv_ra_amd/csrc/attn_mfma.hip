@@ -46,6 +46,10 @@ enum TlSlot {
   TL_P0W = 18,     // + pass (0, 1): the pass's LDS writes and barrier done, wave 0
   TL_P0R = 20,     // + pass: wave 0's sums and stores of the pass issued
   TL_END = 24,     // + wave: the wave's last store issued
+  TL_PLAN = 32,    // wave 0 has its partition and page ranges
+  TL_IDISS = 33,   // wave 0 has requested its page ids and query loads
+  TL_IDLAND = 34,  // wave 0's page ids have landed (early page request only)
+  TL_PGISS = 35,   // wave 0 has requested its first ring pages (early page request only)
 };
 #define TL_MARK(slot)                                                                      \
   do {                                                                                     \
@@ -600,23 +604,62 @@ __device__ __forceinline__ void pv_pair(Acc<KV, D, NT>& acc, const u32x4 (&va)[G
 template <int KV, int D, int NT>
 constexpr int kWavesPerSimd = (NT == 1 && Geo<KV, D>::NRING * Geo<KV, D>::NSL <= 8) ? 4 : 2;
 
+// The cross-wave merge of O.  A wave's O is C = NT * MT chunks of one f32x4
+// per lane (1 KiB per wave): chunk q = nt * MT + j, with i = j / (MT / 4) and
+// k = j % (MT / 4), holds acc.o[4k .. 4k + 3][nt][i], the dims
+// (4 kgrp + i) * MT + 4k .. + 4 of row nt * 16 + ncol: four consecutive dims,
+// stored by the lane in one 16-byte write.  The chunks cross LDS
+// unscaled in at most two passes, chunks [0, CA) and then [CA, C).  Within a
+// pass a wave keeps its chunks in slabs of its own: the first R in its page
+// ring, the next X in an area past all the rings.  So the first pass is stored
+// as soon as the wave's own page loop ends, while other waves still stream.
+// Chunk q of a pass is summed by wave q % kWaves (each SIMD then sums the
+// same number of chunks when a pass holds a multiple of 4).
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+
+template <int KV, int D, int NT>
+struct MergePlan {
+  using G = Geo<KV, D>;
+  static constexpr int R = G::NRING * G::NSL;
+  static constexpr int C = NT * G::MT;
+  // LDS of one workgroup: the CU's 160 KiB over the workgroups it holds
+  static constexpr int kWgPerCu = kWavesPerSimd<KV, D, NT> * 4 / kWaves;
+  static constexpr int kLimit = 163840 / kWgPerCu;
+  // the kernel's other LDS arrays, with slack for their alignment
+  static constexpr int kOther = 2 * (2 * NT * 16 * kWaves * 4) + kWaves * 2 * 64 * 4 +
+                                (KV == KV_I8T ? kWaves * G::NRING * 32 * 4 : 16) + 2 * kWaves * 4 +
+                                NT * G::KS * kWave * 16 + 256;
+  static constexpr int kMaxPerWave = (kLimit - kOther) / (kWaves * kSlab);
+  static constexpr int kFit = (kMaxPerWave / 4) * 4;
+  static constexpr int CA = C <= kMaxPerWave ? C : (kFit > R ? kFit : R);
+  static constexpr int X = CA > R ? CA - R : 0;
+  static constexpr int CB = C - CA;
+  static constexpr int kSlabs = kWaves * (R + X);
+  static_assert(CB <= CA, "two passes hold every chunk");
+  static_assert(kSlabs * kSlab + kOther <= kLimit, "LDS budget");
+  // first slab of wave w's chunk c (index within its pass)
+  static __device__ __forceinline__ int slab(int w, int c) {
+    return c < R ? w * R + c : kWaves * R + w * X + (c - R);
+  }
+};
+
 template <int KV, int D, int NT, bool NTP>
 __global__ void __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<KV, D, NT>)))
 attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
   using G = Geo<KV, D>;
-  // LDS: the per-wave page rings, reused for the cross-wave merge of O
-  constexpr int kRingBytes = kWaves * G::NRING * G::NSL * kSlab;
-  // merge buffer: per pass, (nt, i) pairs x waves x lanes x MT floats
-  constexpr int kPairs = 2 * NT;
-  constexpr int kMergeBytes = kPairs * kWaves * kWave * G::MT * 4;
-  constexpr int kRawBytes = kRingBytes > kMergeBytes ? kRingBytes : kMergeBytes;
-  __shared__ __attribute__((aligned(16))) uint8_t sm_raw[kRawBytes / kSlab][kSlab];
-  __shared__ f32x4 sm_ml[2][NT * 16][kWaves / 4];   // per row: the 8 waves' m (l), read as 2 x 16 B
+  using MP = MergePlan<KV, D, NT>;
+  // LDS: the per-wave page rings, then the merge's extra slabs (see MergePlan)
+  __shared__ __attribute__((aligned(16))) uint8_t sm_raw[MP::kSlabs][kSlab];
+  __shared__ f32x4 sm_m[NT * 16][kWaves / 4];       // per row: the waves' running maxima
+  __shared__ f32x4 sm_fs[2][NT * 16][kWaves / 4];   // per row: the waves' O weights f (x vref) and f * l
   __shared__ int32_t sm_ids[kWaves][2][64];
   // per-token INT8: each ring slot's 16 K and 16 V scales
   __shared__ __attribute__((aligned(16))) float sm_scl[KV == KV_I8T ? kWaves * G::NRING * 32 : 4];
-  __shared__ int32_t sm_bad[kWaves];
-  // RoPE on the fused path: the workgroup's rotated query fragments, [nt][ks][lane]
+  __shared__ __attribute__((aligned(16))) int32_t sm_bad[kWaves];
+  // the workgroup's query fragments, [nt][ks][lane] in operand order
   __shared__ f16x8 sm_q[NT][G::KS][kWave];
 
   // one field of each 64-byte line of the launch arguments, so that the
@@ -646,7 +689,7 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
     TL_VALUE(TL_UNIT, ((uint64_t)u.b << 32) | ((uint64_t)u.h << 24) | ((uint64_t)u.rg << 16) | (uint64_t)u.s);
   }
 #endif
-  const int32_t g = a.hq / a.hkv;
+  const int32_t g = (int32_t)a.fd_g.d;
   const int32_t q_len = q1 - q0;
   const int32_t rows = g * q_len;
   if (rows == 0) return;
@@ -659,8 +702,8 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
   // it can see: a long block (chunked prefill) skips pages past its last query
   // and masks only pages past its first
   SeqFrame frg = fr;
-  frg.pmin = fr.pmin + row0 / g;
-  frg.pmax = fr.pmin + (min(row0 + kMfmaRowsPerBlock, rows) - 1) / g;
+  frg.pmin = fr.pmin + (int32_t)fdiv(a.fd_g, (uint32_t)row0);
+  frg.pmax = fr.pmin + (int32_t)fdiv(a.fd_g, (uint32_t)(min(row0 + kMfmaRowsPerBlock, rows) - 1));
 
   // partition and visible pages
   int32_t lo = 0, hi = 0;
@@ -682,6 +725,7 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
   }
   const int32_t npages = pg.count();
   const int32_t* bt_row = a.block_tables + (int64_t)u.b * a.bt_stride;
+  if (wave == 0) TL_MARK(TL_PLAN);
 
   // first two chunks of the wave's page ids (DMA into LDS)
   int32_t (*sm_id)[64] = sm_ids[wave];
@@ -716,8 +760,9 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
   for (int nt = 0; nt < NT; ++nt) {
     const int32_t r = row0 + nt * 16 + ncol;
     qlive[nt] = r < rows && !bad;
-    pos[nt] = fr.pmin + (qlive[nt] ? r / g : 0);
-    const int64_t qtok = qlive[nt] ? q0 + r / g : 0, qhead = qlive[nt] ? u.h * g + r % g : 0;
+    const int32_t ri = (int32_t)fdiv(a.fd_g, (uint32_t)r), rj = r - ri * g;   // query token, head in group
+    pos[nt] = fr.pmin + (qlive[nt] ? ri : 0);
+    const int64_t qtok = qlive[nt] ? q0 + ri : 0, qhead = qlive[nt] ? u.h * g + rj : 0;
     qp[nt] = reinterpret_cast<const uint16_t*>(a.q) + qtok * a.q_stride + qhead * D + kgrp * (D / 4);
   }
   if (a.rope == nullptr) {
@@ -732,6 +777,7 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
       __builtin_amdgcn_global_load_lds(src + 8 * ks, (lds_u8*)&sm_q[qt][ks][0], 16, 0, 0);
     }
   }
+  if (wave == 0) TL_MARK(TL_IDISS);
   // the fused store of the query tokens' own K/V (decode and verify blocks)
   bool stored = false;
   if (a.new_k != nullptr && !bad) stored = store_new_tokens<KV, D>(a, u.h, q0, q_len, fr.pmin, lo, hi);
@@ -746,11 +792,13 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
   IdRing ids{0, 0};
   if (early) {
     wait_vmcnt<kQOps>();   // the id chunks, older than this wave's kQOps query loads, have landed
+    if (wave == 0) TL_MARK(TL_IDLAND);
     ids.cur = read_id(sm_id[0], lane);
 #pragma unroll
     for (int j = 0; j < NR; ++j)
       if (j < my_pages)
         issue_page<KV, D, NTP>(ring + j * G::NSL, scl + j * 32, ids, sm_id, a, pg, ws, j, bt_row, u.h, lane, bad);
+    if (wave == 0) TL_MARK(TL_PGISS);
     // this wave's query loads, older than the pages just requested; then
     // every wave's (a plain barrier: the pages stay in flight)
     if (my_pages >= NR)
@@ -799,8 +847,10 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
       const int d0 = 8 * ch;
       f16x8 outv = {0, 0, 0, 0, 0, 0, 0, 0};
       if (r < rows && !bad) {
-        const int64_t tok = q0 + r / g;
-        const uint16_t* rowp = reinterpret_cast<const uint16_t*>(a.q) + tok * a.q_stride + (int64_t)(u.h * g + r % g) * D;
+        const int32_t ri = (int32_t)fdiv(a.fd_g, (uint32_t)r);
+        const int64_t tok = q0 + ri;
+        const uint16_t* rowp =
+            reinterpret_cast<const uint16_t*>(a.q) + tok * a.q_stride + (int64_t)(u.h * g + r - ri * g) * D;
         float x[8];
         src8_to_f32(load16(rowp + d0), a.q_bf16, x);
         const int64_t rp = a.positions[tok];
@@ -913,8 +963,11 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
   const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   const int kgrp_e = lane_e >> 4;
   const int ncol_e = lane_e & 15;
-  // ---- combine the waves.  Every wave publishes its rows' (m, l) and its
-  // bad flag, then rescales its O to the common row maximum.
+  // ---- combine the waves (MergePlan).  (1) Every wave publishes its rows'
+  // running maxima and its bad flag, and stores the first pass's chunks of its
+  // O, unscaled, into its own slabs: its ring reads have all returned.
+  f32x4* slabs = reinterpret_cast<f32x4*>(&sm_raw[0][0]);   // [slab][lane]
+  float lrow[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     float l;
@@ -925,136 +978,155 @@ attn_mfma_kernel(AttnLaunch a, int32_t row_groups) {
       l += __shfl_xor(l, 16);
       l += __shfl_xor(l, 32);
     }
-    if (kgrp_e == 0) {
-      reinterpret_cast<float*>(&sm_ml[0][nt * 16 + ncol_e][0])[wave] = acc.m[nt];
-      reinterpret_cast<float*>(&sm_ml[1][nt * 16 + ncol_e][0])[wave] = l;
-    }
+    lrow[nt] = l;
+    if (kgrp_e == 0) reinterpret_cast<float*>(&sm_m[nt * 16 + ncol_e][0])[wave] = acc.m[nt];
   }
   if (lane_e == 0) sm_bad[wave] = bad ? 1 : 0;
+  wait_lgkmcnt0();
+#pragma unroll
+  for (int q = 0; q < MP::CA; ++q) {
+    const int nt = q / G::MT, j = q % G::MT, i = j / (G::MT / 4), k = j % (G::MT / 4);
+    slabs[MP::slab(wave, q) * kWave + lane_e] =
+        f32x4{acc.o[4 * k][nt][i], acc.o[4 * k + 1][nt][i], acc.o[4 * k + 2][nt][i], acc.o[4 * k + 3][nt][i]};
+  }
   __syncthreads();
   if (wave == 0) TL_MARK(TL_COMB);
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) bad = bad || sm_bad[w] != 0;
-  float Mrow[NT], Lrow[NT], fself[NT];
+  // (2) Every wave takes the rows' common maxima M and publishes its own
+  // weights: f = 2^((m - M) c) for its O (times its V reference for
+  // per-token INT8, whose O is in units of it) and f * l for the row sums.
+  {
+    const int4 b4a = *reinterpret_cast<const int4*>(&sm_bad[0]);
+    bad = bad || (b4a.x | b4a.y | b4a.z | b4a.w) != 0;
+    if constexpr (kWaves == 8) {
+      const int4 b4b = *reinterpret_cast<const int4*>(&sm_bad[4]);
+      bad = bad || (b4b.x | b4b.y | b4b.z | b4b.w) != 0;
+    }
+  }
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int rr = nt * 16 + ncol_e;
-    float mw[kWaves], lw[kWaves];
-#pragma unroll
-    for (int q = 0; q < kWaves / 4; ++q) {
-      const f32x4 m4 = sm_ml[0][rr][q], l4 = sm_ml[1][rr][q];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        mw[4 * q + j] = m4[j];
-        lw[4 * q + j] = l4[j];
-      }
-    }
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mw[w]);
-    float L = 0.0f;
-    fself[nt] = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = (mw[w] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((mw[w] - M) * c);
-      L += f * lw[w];
-      if (w == wave) fself[nt] = f;
+    for (int qd = 0; qd < kWaves / 4; ++qd) {
+      const f32x4 m4 = sm_m[rr][qd];
+      M = fmaxf(M, fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
     }
-    Mrow[nt] = M;
-    Lrow[nt] = L;
-    if constexpr (KV == KV_I8T) fself[nt] *= acc.vref;   // O back from units of the wave's reference
+    float f = acc.m[nt] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((acc.m[nt] - M) * c);
+    const float fl = f * lrow[nt];
+    if constexpr (KV == KV_I8T) f *= acc.vref;
+    if (kgrp_e == 0) {
+      reinterpret_cast<float*>(&sm_fs[0][rr][0])[wave] = f;
+      reinterpret_cast<float*>(&sm_fs[1][rr][0])[wave] = fl;
+    }
   }
-  if (wave == 0) TL_MARK(TL_ML);
-
-  // ---- reduce-scatter of O through LDS, in two passes over the lane_e's
-  // accumulator components i (pass p: i = 2p, 2p + 1).  The lane_e's values
-  // acc.o[0..MT)[nt][i] are the MT consecutive dims (4 kgrp_e + i) * MT .. + MT of
-  // row nt * 16 + ncol_e; every wave stores them, then wave w < 2 NT sums pair
-  // w = (nt, i) over the waves in wave order and writes that slice of the
-  // output (same lanes, so the row and its (M, L) are the lane_e's own).
-  f32x4* red = reinterpret_cast<f32x4*>(&sm_raw[0][0]);   // [kPairs][kWaves][MT / 4][kWave]
+  __syncthreads();
+  if (wave == 0) {
+    TL_MARK(TL_ML);
+    TL_MARK(TL_P0W);
+  }
+  // (3) Sum chunk q over the waves in wave order, weighted, and write that
+  // slice of the output (out and lse, or the partition's partials).  A wave's
+  // chunks of a pass are summed together (their LDS reads in flight at once),
+  // then written.
   const float vs = a.v_scale;
+  const auto sum_chunk = [&](int q, int cpass, float (&v)[4], float& L) {
+    const int rr = (q / G::MT) * 16 + ncol_e;
+    float fw[kWaves];
+    L = 0.0f;
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
+    for (int qd = 0; qd < kWaves / 4; ++qd) {
+      const f32x4 f4 = sm_fs[0][rr][qd], l4 = sm_fs[1][rr][qd];
 #pragma unroll
-    for (int pr = 0; pr < kPairs; ++pr) {
-      const int nt = pr >> 1, i = 2 * p + (pr & 1);
-      f32x4* dst = red + (pr * kWaves + wave) * (G::MT / 4) * kWave + lane_e;
+      for (int t = 0; t < 4; ++t) {
+        fw[4 * qd + t] = f4[t];
+        L += l4[t];
+      }
+    }
+    f32x4 x[kWaves];
 #pragma unroll
-      for (int k = 0; k < G::MT / 4; ++k)
-        dst[k * kWave] =
-            f32x4{acc.o[4 * k][nt][i], acc.o[4 * k + 1][nt][i], acc.o[4 * k + 2][nt][i], acc.o[4 * k + 3][nt][i]} *
-            fself[nt];
+    for (int w = 0; w < kWaves; ++w) x[w] = slabs[MP::slab(w, cpass) * kWave + lane_e];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) v[t] = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) v[t] = fmaf(x[w][t], fw[w], v[t]);
+  };
+  const auto emit_chunk = [&](int q, float (&v)[4], float L) {
+    const int nt = q / G::MT, j = q % G::MT, i = j / (G::MT / 4), k = j % (G::MT / 4);
+    const int rr = nt * 16 + ncol_e;
+    const int32_t r = row0 + rr;
+    if (r < rows) {
+      const int32_t qi = (int32_t)fdiv(a.fd_g, (uint32_t)r), hj = r - qi * g;
+      const int64_t orow = (int64_t)(q0 + qi) * a.hq + u.h * g + hj;
+      // a row with no visible key has L = 0 (out 0, lse -inf); NaN scores
+      // leave L = NaN, and the row stays NaN in out and lse
+      const float inv = L > 0.0f ? vs / L : (L == L ? 0.0f : __builtin_nanf(""));
+      const int d0 = (4 * kgrp_e + i) * G::MT + 4 * k;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) v[t] = bad ? __builtin_nanf("") : v[t] * inv;
+      if (a.direct) {
+        uint16_t hv[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) hv[t] = a.q_bf16 ? f32_to_bf16(v[t]) : as<uint16_t>((f16)v[t]);
+        u32x2 w2;
+        w2[0] = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
+        w2[1] = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
+        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + orow * D + d0) = w2;
+      } else {
+        float* op = a.part_out + ((int64_t)u.s * a.total_q * a.hq + orow) * D + d0;
+        *reinterpret_cast<f32x4*>(op) = f32x4{v[0], v[1], v[2], v[3]};
+      }
+      if (kgrp_e == 0 && j == 0) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int qd = 0; qd < kWaves / 4; ++qd) {
+          const f32x4 m4 = sm_m[rr][qd];
+          M = fmaxf(M, fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+        }
+        float lse = L > 0.0f ? (M * c + log2f(L)) * kLn2 : (L == L ? -INFINITY : __builtin_nanf(""));
+        if (bad) lse = __builtin_nanf("");
+        if (a.direct) {
+          if (a.lse) a.lse[orow] = lse;
+        } else {
+          a.part_lse[(int64_t)u.s * a.total_q * a.hq + orow] = lse;
+        }
+      }
+    }
+  };
+  // chunks [QA, QB) of a pass: this wave's are QA + wave + t * kWaves
+  const auto reduce_pass = [&](auto qa, auto qb) {
+    constexpr int QA = decltype(qa)::value, QB = decltype(qb)::value;
+    constexpr int kPer = (QB - QA + kWaves - 1) / kWaves;
+    constexpr bool kFull = (QB - QA) % kWaves == 0;
+    float v[kPer][4], L[kPer];
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) {
+      const int q = QA + wave + t * kWaves;
+      if (kFull || q < QB) sum_chunk(q, q - QA, v[t], L[t]);
+    }
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) {
+      const int q = QA + wave + t * kWaves;
+      if (kFull || q < QB) emit_chunk(q, v[t], L[t]);
+    }
+  };
+  reduce_pass(IntC<0>{}, IntC<MP::CA>{});
+  if (wave == 0) TL_MARK(TL_P0R);
+  if constexpr (MP::CB > 0) {
+    // (4) the second pass, through the same slabs once every wave has read
+    // the first
+    __syncthreads();
+#pragma unroll
+    for (int q = MP::CA; q < MP::C; ++q) {
+      const int nt = q / G::MT, j = q % G::MT, i = j / (G::MT / 4), k = j % (G::MT / 4);
+      slabs[MP::slab(wave, q - MP::CA) * kWave + lane_e] =
+          f32x4{acc.o[4 * k][nt][i], acc.o[4 * k + 1][nt][i], acc.o[4 * k + 2][nt][i], acc.o[4 * k + 3][nt][i]};
     }
     __syncthreads();
-    if (wave == 0) TL_MARK(TL_P0W + p);
-    for (int pr = wave; pr < kPairs; pr += kWaves) {
-      const int nt = pr >> 1, i = 2 * p + (pr & 1);
-      float v[G::MT];
-#pragma unroll
-      for (int mt = 0; mt < G::MT; ++mt) v[mt] = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const f32x4* src = red + (pr * kWaves + w) * (G::MT / 4) * kWave + lane_e;
-#pragma unroll
-        for (int k = 0; k < G::MT / 4; ++k) {
-          const f32x4 x = src[k * kWave];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) v[4 * k + j] += x[j];
-        }
-      }
-      // rows of this pair, by the lane_e's own (M, L)
-      float L = 0.0f, M = 0.0f;
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-        if (t == nt) { L = Lrow[t]; M = Mrow[t]; }
-      const int32_t r = row0 + nt * 16 + ncol_e;
-      if (r < rows) {
-        const int32_t qi = r / g, hj = r % g;
-        const int64_t orow = (int64_t)(q0 + qi) * a.hq + u.h * g + hj;
-        // a row with no visible key has L = 0 (out 0, lse -inf); NaN scores
-        // leave L = NaN, and the row stays NaN in out and lse
-        const float inv = L > 0.0f ? vs / L : (L == L ? 0.0f : __builtin_nanf(""));
-        const int d0 = (4 * kgrp_e + i) * G::MT;
-#pragma unroll
-        for (int mt = 0; mt < G::MT; ++mt) v[mt] = bad ? __builtin_nanf("") : v[mt] * inv;
-        if (a.direct) {
-          uint16_t hv[G::MT];
-#pragma unroll
-          for (int mt = 0; mt < G::MT; ++mt) hv[mt] = a.q_bf16 ? f32_to_bf16(v[mt]) : as<uint16_t>((f16)v[mt]);
-          uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + orow * D + d0;
-#pragma unroll
-          for (int k = 0; k < G::MT / 8; ++k) {
-            u32x4 w;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) w[j] = (uint32_t)hv[8 * k + 2 * j] | ((uint32_t)hv[8 * k + 2 * j + 1] << 16);
-            *reinterpret_cast<u32x4*>(op + 8 * k) = w;
-          }
-          if constexpr (G::MT % 8 != 0) {
-            u32x2 w;
-            w[0] = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
-            w[1] = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
-            *reinterpret_cast<u32x2*>(op) = w;
-          }
-        } else {
-          float* op = a.part_out + ((int64_t)u.s * a.total_q * a.hq + orow) * D + d0;
-#pragma unroll
-          for (int k = 0; k < G::MT / 4; ++k)
-            *reinterpret_cast<f32x4*>(op + 4 * k) = f32x4{v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]};
-        }
-        if (kgrp_e == 0 && i == 0) {
-          float lse = L > 0.0f ? (M * c + log2f(L)) * kLn2 : (L == L ? -INFINITY : __builtin_nanf(""));
-          if (bad) lse = __builtin_nanf("");
-          if (a.direct) {
-            if (a.lse) a.lse[orow] = lse;
-          } else {
-            a.part_lse[(int64_t)u.s * a.total_q * a.hq + orow] = lse;
-          }
-        }
-      }
-    }
-    if (wave == 0) TL_MARK(TL_P0R + p);
-    if (p == 0) __syncthreads();   // the second pass reuses the buffer
+    if (wave == 0) TL_MARK(TL_P0W + 1);
+    reduce_pass(IntC<MP::CA>{}, IntC<MP::C>{});
+    if (wave == 0) TL_MARK(TL_P0R + 1);
   }
   TL_MARK(TL_END + wave);
 }
@@ -1088,12 +1160,17 @@ hipError_t launch_d(const AttnLaunch& a, int nt, int32_t row_groups, hipStream_t
 
 }  // namespace
 
-hipError_t launch_attn_mfma(const AttnLaunch& a, hipStream_t s) {
-  const int32_t g = a.hq / a.hkv;
-  const int32_t rows_max = g * a.max_q_len;
+hipError_t launch_attn_mfma(const AttnLaunch& a0, hipStream_t s) {
+  const int32_t g = a0.hq / a0.hkv;
+  const int32_t rows_max = g * a0.max_q_len;
   const int32_t rows_blk = rows_max < kMfmaRowsPerBlock ? rows_max : kMfmaRowsPerBlock;
   const int nt = (rows_blk + 15) / 16;
   const int32_t row_groups = (rows_max + kMfmaRowsPerBlock - 1) / kMfmaRowsPerBlock;
+  AttnLaunch a = a0;
+  a.fd_g = make_fastdiv((uint32_t)g);
+  a.fd_batch = make_fastdiv((uint32_t)a.batch);
+  a.fd_hkv = make_fastdiv((uint32_t)a.hkv);
+  a.fd_rg = make_fastdiv((uint32_t)row_groups);
   switch (a.kv) {
     case KV_F16: return launch_d<KV_F16>(a, nt, row_groups, s);
     case KV_E4M3: return launch_d<KV_E4M3>(a, nt, row_groups, s);

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fastdiv.h"
+
 namespace ra {
 
 // KV_I8T: INT8 codes with fp32 scales per (token, head) in separate planes.
@@ -126,6 +128,9 @@ struct AttnLaunch {
   int32_t rope_max_pos;
   int32_t rot;
   const int64_t* positions;
+  // divisions by launch constants (filled by the decode/verify launcher):
+  // g = hq / hkv, batch, hkv and the row groups per unit
+  FastDiv fd_g, fd_batch, fd_hkv, fd_rg;
 };
 
 // Rows of a (sequence, KV head) unit: g * q_len, in 16-row matrix-core tiles
