@@ -41,7 +41,7 @@ PEAK_F16_TFLOPS = 2500.0      # dense fp16 matrix-core peak (the path's MFMA dty
 POOL_ROTATION_BYTES = 1 << 30
 KERNEL_SOURCES = ["paged_quantized_kv_ra_amd/csrc/attn_mfma.hip", "paged_quantized_kv_ra_amd/csrc/attn_prefill.hip",
                   "paged_quantized_kv_ra_amd/csrc/attn_common.h", "paged_quantized_kv_ra_amd/csrc/ra_device.h",
-                  "paged_quantized_kv_ra_amd/csrc/ra_internal.h"]
+                  "paged_quantized_kv_ra_amd/csrc/ra_internal.h", "paged_quantized_kv_ra_amd/csrc/fastdiv.h"]
 
 
 def kernel_source_hash():

@@ -8,11 +8,14 @@
 // computed here at store time (ReVolta README, "Weight and KV formats", INT8
 // KV), into 16-token pages ("ReVolta 0.1.3", "Known issues").
 //
-// One thread handles 8 consecutive dimensions of one (token, head): it reads
-// 16 bytes of K and 16 of V, quantises with a correctly rounded fp32 divide,
-// writes the K codes as one 8- or 16-byte store (a K row slice is contiguous
-// in the layout) and the V codes as single-element stores (V interleaves four
-// tokens per dimension).
+// One thread handles 8 consecutive dimensions of one head for four
+// consecutive source tokens (a token quad): it reads 16 bytes of K and 16 of V
+// per token, quantises with a correctly rounded fp32 divide, and writes each
+// token's K codes as one 8- or 16-byte store (a K row slice is contiguous in
+// the layout).  V interleaves four tokens per dimension: when the quad's slots
+// are the four tokens of one 4-token group of a page (a prompt or a bulk fill
+// written in order), the V codes go out as whole 16-byte pieces
+// (store_v_quad); otherwise each element is stored on its own.
 #include "ra_device.h"
 #include "ra_internal.h"
 
@@ -28,55 +31,80 @@ __global__ void __launch_bounds__(256) kv_store_kernel(StoreLaunch a) {
                "s"(a.k_cache), "s"(a.v_cache), "s"(a.num_pages), "s"(a.hkv), "s"(a.k_scale), "s"(a.v_scale),
                "s"(gridDim.x), "s"(blockDim.x), "s"(a.k_scales), "s"(a.v_scales));
   // the host guarantees num_tokens * hkv * CH < 2^31
-  const int32_t units = (int32_t)(a.num_tokens * a.hkv * CH);
+  const int64_t T = a.num_tokens;
+  const int32_t units = (int32_t)((T + 3) / 4 * a.hkv * CH);
   const int64_t limit = a.num_pages * kPage;
   for (int32_t u = blockIdx.x * blockDim.x + threadIdx.x; u < units; u += gridDim.x * blockDim.x) {
     const int c = u % CH;
     const int32_t th = u / CH;
     const int h = th % a.hkv;
-    const int32_t t = th / a.hkv;
+    const int64_t t0 = 4 * (int64_t)(th / a.hkv);   // the quad's first source token
+    const int nt = (int)min((int64_t)4, T - t0);
     const int d0 = c * 8;
-    // the source rows and the slot are requested together
-    const uint16_t* ksrc = reinterpret_cast<const uint16_t*>(a.k) + t * a.k_stride + (int64_t)h * D + d0;
-    const uint16_t* vsrc = reinterpret_cast<const uint16_t*>(a.v) + t * a.v_stride + (int64_t)h * D + d0;
-    const u32x4 kr = load16(ksrc);
-    const u32x4 vr = load16(vsrc);
-    const int64_t slot = a.slots[t];
-    asm volatile("" ::"v"(kr), "v"(vr), "v"(slot));   // all three in flight before the first wait
-    if (slot < 0 || slot >= limit) continue;
-    const int64_t page = slot >> 4;
-    const int tp = (int)(slot & 15);
-    float kf[8], vf[8];
+    // the quad's source rows and slots are requested together (a short last
+    // quad repeats its last token; only tokens j < nt are stored)
+    u32x4 kr[4], vr[4];
+    int64_t slot[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint16_t kb = (uint16_t)(kr[i >> 1] >> (16 * (i & 1)));
-      const uint16_t vb = (uint16_t)(vr[i >> 1] >> (16 * (i & 1)));
-      if constexpr (BF16) {
-        kf[i] = bf16_to_f32(kb);
-        vf[i] = bf16_to_f32(vb);
-      } else {
-        kf[i] = (float)as<f16>(kb);
-        vf[i] = (float)as<f16>(vb);
-      }
+    for (int j = 0; j < 4; ++j) {
+      const int64_t t = t0 + min(j, nt - 1);
+      kr[j] = load16(reinterpret_cast<const uint16_t*>(a.k) + t * a.k_stride + (int64_t)h * D + d0);
+      vr[j] = load16(reinterpret_cast<const uint16_t*>(a.v) + t * a.v_stride + (int64_t)h * D + d0);
+      slot[j] = a.slots[t];
     }
-    const int64_t blk = (page * a.hkv + h) * (int64_t)(kPage * D * E);
-    uint8_t* kc = reinterpret_cast<uint8_t*>(a.k_cache) + blk;
-    uint8_t* vc = reinterpret_cast<uint8_t*>(a.v_cache) + blk;
-
-    // per-token INT8: the (token, head) row's scale is max |x| / 127 over its
+    asm volatile("" ::"v"(kr[0]), "v"(kr[1]), "v"(kr[2]), "v"(kr[3]), "v"(vr[0]), "v"(vr[1]), "v"(vr[2]),
+                 "v"(vr[3]), "v"(slot[0]), "v"(slot[1]), "v"(slot[2]), "v"(slot[3]));   // all in flight
+    float kf[4][8], vf[4][8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint16_t kb = (uint16_t)(kr[j][i >> 1] >> (16 * (i & 1)));
+        const uint16_t vb = (uint16_t)(vr[j][i >> 1] >> (16 * (i & 1)));
+        if constexpr (BF16) {
+          kf[j][i] = bf16_to_f32(kb);
+          vf[j][i] = bf16_to_f32(vb);
+        } else {
+          kf[j][i] = (float)as<f16>(kb);
+          vf[j][i] = (float)as<f16>(vb);
+        }
+      }
+    // per-token INT8: each (token, head) row's scale is max |x| / 127 over its
     // CH threads (consecutive lanes of one wave, all active or all skipped)
-    float ks = a.k_scale, vs = a.v_scale;
-    if constexpr (KV == KV_I8T) {
-      ks = row_absmax(kf, CH) / 127.0f;   // correctly rounded (built with -fhip-fp32-correctly-rounded-divide-sqrt)
-      vs = row_absmax(vf, CH) / 127.0f;
-      if (c == 0) {
-        const int64_t si = (page * a.hkv + h) * kPage + tp;
-        a.k_scales[si] = ks;
-        a.v_scales[si] = vs;
+    float ks[4], vs[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ks[j] = a.k_scale;
+      vs[j] = a.v_scale;
+      if constexpr (KV == KV_I8T) {
+        ks[j] = row_absmax(kf[j], CH) / 127.0f;   // correctly rounded (built with -fhip-fp32-correctly-rounded-divide-sqrt)
+        vs[j] = row_absmax(vf[j], CH) / 127.0f;
       }
     }
-    store_row8<KV, D>(kc, tp, d0, kf, ks, false);
-    store_row8<KV, D>(vc, tp, d0, vf, vs, true);
+    uint8_t* const k0 = reinterpret_cast<uint8_t*>(a.k_cache);
+    uint8_t* const v0 = reinterpret_cast<uint8_t*>(a.v_cache);
+    const bool whole = nt == 4 && slot[0] >= 0 && slot[0] + 3 < limit && (slot[0] & 3) == 0 &&
+                       slot[1] == slot[0] + 1 && slot[2] == slot[0] + 2 && slot[3] == slot[0] + 3;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j >= nt || slot[j] < 0 || slot[j] >= limit) continue;
+      const int64_t page = slot[j] >> 4;
+      const int tp = (int)(slot[j] & 15);
+      const int64_t blk = (page * a.hkv + h) * (int64_t)(kPage * D * E);
+      if constexpr (KV == KV_I8T) {
+        if (c == 0) {
+          const int64_t si = (page * a.hkv + h) * kPage + tp;
+          a.k_scales[si] = ks[j];
+          a.v_scales[si] = vs[j];
+        }
+      }
+      store_row8<KV, D>(k0 + blk, tp, d0, kf[j], ks[j], false);
+      if (!whole) store_row8<KV, D>(v0 + blk, tp, d0, vf[j], vs[j], true);
+    }
+    if (whole) {
+      const int64_t page = slot[0] >> 4;
+      store_v_quad<KV, D>(v0 + (page * a.hkv + h) * (int64_t)(kPage * D * E), (int)(slot[0] & 15) >> 2, d0, vf, vs);
+    }
   }
 }
 
@@ -154,7 +182,7 @@ dim3 grid_for(int64_t units) {
 
 hipError_t launch_kv_store(const StoreLaunch& a, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
-  const dim3 g = grid_for(a.num_tokens * a.hkv * (a.head_dim / 8)), b(256);
+  const dim3 g = grid_for((a.num_tokens + 3) / 4 * a.hkv * (a.head_dim / 8)), b(256);
   switch (a.kv) {
     case KV_F16: return store_dispatch_d<KV_F16>(a, s, g, b);
     case KV_E4M3: return store_dispatch_d<KV_E4M3>(a, s, g, b);

@@ -175,6 +175,41 @@ __device__ __forceinline__ void store_row8(uint8_t* blk, int tp, int d0, const f
 }
 
 
+// Quantise dims d0 .. d0 + 7 (d0 a multiple of 8) of the four tokens of token
+// quad gq of one page (tokens 4 gq .. 4 gq + 3, x[j] the row of token
+// 4 gq + j, scale[j] its scale) and write their V codes.  The four tokens
+// interleave per dim in the layout, so together they fill whole 16-byte
+// pieces: 2 E of them in one lane's row at D = 128, E in each of two lanes
+// at D = 64, each written with one store.
+template <int KV, int D>
+__device__ __forceinline__ void store_v_quad(uint8_t* blk, int gq, int d0, const float (&x)[4][8],
+                                             const float (&scale)[4]) {
+  constexpr int E = KV == KV_F16 ? 2 : 1;
+  constexpr int W = D / 16;                     // dims per lane row
+  constexpr int NL = W >= 8 ? 1 : 8 / W;        // lane rows the 8 dims span
+  constexpr int NP = 2 * E / NL;                // 16-byte pieces per lane row
+  static_assert(W == 8 || W == 4, "head_dim 128 or 64");
+  u32x4 piece[NL][NP];
+#pragma unroll
+  for (int l = 0; l < NL; ++l)
+#pragma unroll
+    for (int p = 0; p < NP; ++p) piece[l][p] = u32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // v_elem_offset(4 gq + j, d0 + i): lane row 16 gq + (d0 + i) / W, byte b
+      const int l = W >= 8 ? 0 : i / W;
+      const int b = ((i % W) * 4 + j) * E;
+      piece[l][b >> 4][(b & 15) >> 2] |= encode_code<KV>(x[j][i], scale[j]) << (8 * (b & 3));
+    }
+  const int lane0 = 16 * gq + d0 / W;
+#pragma unroll
+  for (int l = 0; l < NL; ++l)
+#pragma unroll
+    for (int p = 0; p < NP; ++p) *reinterpret_cast<u32x4*>(blk + p * 1024 + (lane0 + l) * 16) = piece[l][p];
+}
+
 // ---------------------------------------------------------------------------
 // Rotary position embedding (half-split pairing, dim i with i + R/2): the
 // pair turns as y1 = x1 c - x2 s, y2 = x2 c + x1 s, evaluated as written in

@@ -204,3 +204,72 @@ def test_store_int8_token_codes_and_scales_bit_exact(D, src):
             src_x = w.tokens_k if which == 0 else w.tokens_v
             want = OC.roundtrip(OC.source_to_f32(src_x[rows], w.src_dtype), "int8_tok")
             assert np.array_equal(got.cpu().numpy().view(np.uint32), want.view(np.uint32)), (b, which)
+
+
+def _quad_mix_slots(pages):
+    """Slots of 43 source tokens (10 quads and a short tail) that exercise the
+    store's whole-quad V path next to every case that must not take it."""
+    s = []
+    s += [5 * 16 + i for i in range(16)]                  # quads 0-3: one page, in order
+    s += [2 * 16 + 4 + i for i in range(4)]               # quad 4: whole group 1 of page 2
+    s += [2 * 16 + 9 + i for i in range(4)]               # quad 5: consecutive but misaligned
+    s += [3 * 16 + 0, -1, 3 * 16 + 2, 3 * 16 + 3]        # quad 6: a skipped slot inside
+    s += [3 * 16 + 11 - i for i in range(4)]              # quad 7: one group, reversed
+    s += [4 * 16 + 12, 4 * 16 + 13, 4 * 16 + 14, 6 * 16 + 15]   # quad 8: last token elsewhere
+    s += [pages * 16 - 4 + i for i in range(4)]           # quad 9: the pool's last group
+    s += [7 * 16 + i for i in range(3)]                   # tail: an aligned but short quad
+    assert len(s) == 43 and len({x for x in s if x >= 0}) == 42
+    return np.array(s, np.int64)
+
+
+@pytest.mark.parametrize("kv", ["f16", "e4m3", "int8", "int8_tok"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("src", ["f16", "bf16"])
+def test_store_token_quads_mixed(kv, D, src):
+    """A source quad whose slots are one 4-token group of a page writes its V
+    codes as whole 16-byte pieces; every other quad stores element by
+    element.  Either way every cache byte (and per-token scale) equals the
+    oracle's scatter, and bytes of unwritten slots keep their sentinel."""
+    hkv, pages = 2, 10
+    slots = _quad_mix_slots(pages)
+    T = slots.size
+    rng = np.random.default_rng(D + (kv == "f16") + 7 * (src == "bf16"))
+    x32 = rng.standard_normal((2, T, hkv, D)).astype(np.float32)
+    x32[1, 9, 1] *= 1e-3                                  # rows of very different magnitude
+    x32[0, 17, 0] = 0.0                                   # and a zero row (per-token scale 0)
+    if src == "f16":
+        xs = x32.astype(np.float16)
+        kt, vt = (torch.from_numpy(xs[i]).cuda() for i in range(2))
+    else:
+        xs = (x32.view(np.uint32) >> 16).astype(np.uint16)
+        kt, vt = (torch.from_numpy(xs[i].view(np.int16)).cuda().view(torch.bfloat16) for i in range(2))
+    e = 2 if kv == "f16" else 1
+    sentinel = 0x3C01 if kv == "f16" else 0xA5
+    kc = P.new_cache(pages, hkv, D, kv, fill=sentinel)
+    vc = P.new_cache(pages, hkv, D, kv, fill=sentinel)
+    st = torch.from_numpy(slots).cuda()
+    if kv == "int8_tok":
+        ksp, vsp = P.new_scale_plane(pages, hkv), P.new_scale_plane(pages, hkv)
+        P.kv_store(kt, vt, st, kc, vc, kv, k_scales=ksp, v_scales=vsp)
+    else:
+        P.kv_store(kt, vt, st, kc, vc, kv, 0.0130004883, 0.02)
+    torch.cuda.synchronize()
+    log(f"quad mix {kv} D={D} {src}: {T} tokens")
+    nbytes = pages * hkv * 16 * D * e
+    for which, i, cache in (("k", 0, kc), ("v", 1, vc)):
+        xf = OC.source_to_f32(xs[i], src)
+        if kv == "f16":
+            cache0 = np.frombuffer(np.full(nbytes // 2, sentinel, np.uint16).tobytes(), np.uint8).copy()
+        else:
+            cache0 = np.full(nbytes, sentinel, np.uint8)
+        if kv == "int8_tok":
+            codes, sc = OC.quantize_per_token(xf)
+            plane = (ksp if which == "k" else vsp).cpu().numpy().reshape(-1)
+            want_plane = OL.scatter_scales(np.full(pages * hkv * 16, np.nan, np.float32), sc, slots, hkv)
+            assert np.array_equal(plane.view(np.uint32), want_plane.view(np.uint32)), f"{which}: scales differ"
+        else:
+            codes = OC.quantize(xf, kv, 0.0130004883 if which == "k" else 0.02)
+        want = OL.scatter(cache0, codes, slots, which, hkv, D, kv)
+        got = _gpu_bytes(cache)
+        diff = np.nonzero(got != want)[0]
+        assert diff.size == 0, f"{which}: {diff.size} bytes differ, first at {diff[:8]}"
