@@ -222,18 +222,13 @@ def _quad_mix_slots(pages):
     return np.array(s, np.int64)
 
 
-@pytest.mark.parametrize("kv", ["f16", "e4m3", "int8", "int8_tok"])
-@pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("src", ["f16", "bf16"])
-def test_store_token_quads_mixed(kv, D, src):
-    """A source quad whose slots are one 4-token group of a page writes its V
-    codes as whole 16-byte pieces; every other quad stores element by
-    element.  Either way every cache byte (and per-token scale) equals the
-    oracle's scatter, and bytes of unwritten slots keep their sentinel."""
-    hkv, pages = 2, 10
-    slots = _quad_mix_slots(pages)
+def _check_store(kv, D, src, slots, pages, seed):
+    """Store random K/V rows at `slots` and compare every cache byte (and
+    per-token scale) with the oracle's scatter into the same sentinel-filled
+    caches."""
+    hkv = 2
     T = slots.size
-    rng = np.random.default_rng(D + (kv == "f16") + 7 * (src == "bf16"))
+    rng = np.random.default_rng(seed)
     x32 = rng.standard_normal((2, T, hkv, D)).astype(np.float32)
     x32[1, 9, 1] *= 1e-3                                  # rows of very different magnitude
     x32[0, 17, 0] = 0.0                                   # and a zero row (per-token scale 0)
@@ -254,7 +249,7 @@ def test_store_token_quads_mixed(kv, D, src):
     else:
         P.kv_store(kt, vt, st, kc, vc, kv, 0.0130004883, 0.02)
     torch.cuda.synchronize()
-    log(f"quad mix {kv} D={D} {src}: {T} tokens")
+    log(f"store {kv} D={D} {src}: {T} tokens")
     nbytes = pages * hkv * 16 * D * e
     for which, i, cache in (("k", 0, kc), ("v", 1, vc)):
         xf = OC.source_to_f32(xs[i], src)
@@ -273,3 +268,29 @@ def test_store_token_quads_mixed(kv, D, src):
         got = _gpu_bytes(cache)
         diff = np.nonzero(got != want)[0]
         assert diff.size == 0, f"{which}: {diff.size} bytes differ, first at {diff[:8]}"
+
+
+@pytest.mark.parametrize("kv", ["f16", "e4m3", "int8", "int8_tok"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("src", ["f16", "bf16"])
+def test_store_token_quads_mixed(kv, D, src):
+    """A small store (one token per thread): every slot pattern of the mix,
+    bytes equal to the oracle's scatter, unwritten bytes keep their sentinel."""
+    _check_store(kv, D, src, _quad_mix_slots(10), 10, D + (kv == "f16") + 7 * (src == "bf16"))
+
+
+@pytest.mark.parametrize("kv", ["f16", "e4m3", "int8_tok"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_store_bulk_token_quads(kv, D):
+    """A bulk store (four tokens per thread: at least 131,072 (token, head)
+    rows).  A group of four source tokens whose slots are one 4-token group
+    of a page writes its V codes as whole 16-byte pieces; every other group
+    (the mix's cases, and a run that only lines up from its second token on)
+    stores element by element.  Every byte equals the oracle's scatter."""
+    pages = 4200
+    mix = _quad_mix_slots(pages)                          # source tokens 0 .. 42
+    # token 43 takes a slot = 3 (mod 4), so the groups from token 44 on are whole
+    bulk = 8 * 16 + 3 + np.arange(65536, dtype=np.int64)
+    slots = np.concatenate([mix, bulk])
+    assert slots.size * 2 >= 131072 and bulk[-1] < (pages - 1) * 16
+    _check_store(kv, D, "f16", slots, pages, 40 + D)
