@@ -280,3 +280,26 @@ def test_int8tok_precision_independent_of_v_magnitude(kind, ql, S):
     out, lse = dw.attn()
     torch.cuda.synchronize()
     _check_all(w, out, lse, f"int8tok V {kind} q_len {ql} S {S}")
+
+
+# Every shape of the cross-wave merge: per KV format and head_dim, one, two and
+# three row tiles (8, 24 and 40 rows per KV head), written directly (one
+# partition: out and lse in the query dtype) or as partials merged afterwards.
+# The merge passes differ between these shapes (one pass in the rings, one pass
+# with slabs past the rings, two passes), and so do the chunk layouts.
+MERGE_CASES = [
+    (f"merge_{kv}_d{D}_q{ql}_S{S}_{qd}", [700, 333], [ql, ql], 16, 2, D, kv, qd, -1, 0, S)
+    for kv in ["f16", "e4m3", "int8", "int8_tok"]
+    for D in [64, 128]
+    for ql in [1, 3, 5]
+    for S, qd in [(1, "bf16"), (3, "f16")]
+]
+
+
+@pytest.mark.parametrize("case", MERGE_CASES, ids=[c[0] for c in MERGE_CASES])
+def test_merge_shapes_match_oracle(case):
+    w = _build(case, seed=31)
+    dw = DeviceWorkload(w)
+    out, lse = dw.attn()
+    torch.cuda.synchronize()
+    _check_all(w, out, lse, case[0])
